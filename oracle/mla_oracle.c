@@ -1,0 +1,384 @@
+/*
+ * CPU oracle for MLA decode over an fp8 latent KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  It shares no
+ * code, header, table or helper with the GPU library: every conversion and
+ * every reduction below is written out from its definition, accumulates in
+ * IEEE double, and runs in plain loops with no blocking or fusion.
+ *
+ * Sources (the pages are vLLM API documentation of the Kimi decode runtime):
+ *   [MLA]   "vllm.models.kimi_k3.amd.specialized_decode.runtime.mla"
+ *           sections `attend`, `m1c_inputs`, `post`, `pre`.
+ *   [VALUE] "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.mla.value"
+ *           classes `MlaValue`, `MlaGate`.
+ * Where the pages leave a step open, the reading taken is named at the
+ * function that takes it.
+ *
+ * Parity status of each function: every function here is pinned by the
+ * CPU tests (closed forms, library routines, brute force, invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_D_LATENT 512 /* kv_lora width: the value part of a cache row */
+#define ORC_D_ROPE 64
+#define ORC_D_QK 576 /* one cache row: 512 latent then 64 rope ([MLA] `pre`) */
+#define ORC_D_V 128  /* per-head output width of W_UV ([VALUE] `MlaValue`) */
+
+/* ---------------------------------------------------------------- codecs */
+
+/* fp8 E4M3 in the OCP "fn" flavour (no infinities): sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; exponent field 0 is subnormal; 0x7F / 0xFF
+ * are NaN.  Reading taken: the cache dtype of [MLA] `attend` is this
+ * format (the one the target GPU converts natively). */
+double orc_fp8_decode(uint8_t b) {
+  int sign = (b >> 7) & 1;
+  int e = (b >> 3) & 0xF;
+  int m = b & 7;
+  double mag;
+  if (e == 0xF && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -6 - 3); /* m/8 * 2^-6 */
+  else
+    mag = ldexp(8.0 + m, e - 7 - 3); /* (1 + m/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+/* Round a double to the nearest value with `p` significant bits whose
+ * exponent is at least `emin` (so subnormals keep a fixed quantum), ties to
+ * even.  No range limit is applied here. */
+static double round_to_precision(double x, int p, int emin) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  frexp(x, &e); /* |x| = f * 2^e with f in [0.5, 1): leading bit is 2^(e-1) */
+  int lead = e - 1;
+  if (lead < emin) lead = emin;
+  double quantum = ldexp(1.0, lead - (p - 1));
+  /* x / quantum is exact (power-of-two scaling); nearbyint rounds ties to
+   * even in the default rounding mode. */
+  return nearbyint(x / quantum) * quantum;
+}
+
+/* Encoder E of the cache write: round to nearest even among fp8 E4M3
+ * values, saturating to +-448, NaN -> 0x7F.  Reading taken: [MLA] `pre`
+ * stores the scaled row in fp8 without saying how it rounds; nearest-even
+ * with saturation is the plain choice. */
+uint8_t orc_fp8_encode(double x) {
+  if (isnan(x)) return 0x7F;
+  int neg = signbit(x) ? 1 : 0;
+  double a = fabs(x);
+  double r = round_to_precision(a, 4, -6);
+  if (r > 448.0) r = 448.0;
+  int code;
+  if (r < ldexp(1.0, -6)) {
+    code = (int)(r / ldexp(1.0, -9)); /* subnormal: r = m * 2^-9, m in 0..7 */
+  } else {
+    int e;
+    double f = frexp(r, &e); /* r = f * 2^e, f in [0.5, 1) */
+    int mant = (int)((2.0 * f - 1.0) * 8.0); /* r = (1 + mant/8) * 2^(e-1) */
+    if (mant == 8) { mant = 0; e += 1; } /* not reached: r has 4 significant bits */
+    code = ((e - 1 + 7) << 3) | mant;
+  }
+  return (uint8_t)(code | (neg << 7));
+}
+
+/* bf16: the upper half of an IEEE binary32. */
+double orc_bf16_decode(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* Round a double to bf16 (8 significant bits, emin -126, overflow -> inf),
+ * ties to even; NaN -> 0x7FC0. */
+uint16_t orc_bf16_round(double x) {
+  if (isnan(x)) return 0x7FC0;
+  double r = round_to_precision(x, 8, -126);
+  /* largest finite bf16 is (2 - 2^-7) * 2^127; beyond it rounds to inf */
+  double maxf = ldexp(255.0, 127 - 7);
+  float f;
+  if (fabs(r) > maxf)
+    f = signbit(x) ? -INFINITY : INFINITY;
+  else
+    f = (float)r; /* exact: r has 8 significant bits and a binary32 range */
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+/* fp4 E2M1 (OCP MX): sign, 2 exponent bits with bias 1, 1 mantissa bit. */
+double orc_e2m1_decode(uint8_t nib) {
+  int sign = (nib >> 3) & 1;
+  int e = (nib >> 1) & 3;
+  int m = nib & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* E8M0 shared scale (OCP MX): 2^(b - 127); 0xFF is NaN. */
+double orc_e8m0_decode(uint8_t b) {
+  if (b == 0xFF) return NAN;
+  return ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------------- kv write */
+
+/* The cache write of [MLA] `pre` (do_kv_cache_update of kv_c and k_pe): new
+ * token i's row is [kv_c (512) | k_pe (64)], each value divided by kv_scale
+ * in binary32 and encoded with E, stored at row slot_mapping[i].  A negative
+ * slot skips the token.  Reading taken: the division is a correctly rounded
+ * binary32 division, as written "x / k_scale". */
+void orc_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                  int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n,
+                  uint8_t* kv_cache, float kv_scale) {
+  for (int32_t i = 0; i < n; ++i) {
+    int64_t slot = slot_mapping[i];
+    if (slot < 0) continue;
+    for (int c = 0; c < ORC_D_QK; ++c) {
+      uint16_t h = c < ORC_D_LATENT ? kv_c[i * kv_c_stride + c]
+                                    : k_pe[i * k_pe_stride + (c - ORC_D_LATENT)];
+      float x = (float)orc_bf16_decode(h);
+      float scaled = x / kv_scale; /* binary32 division */
+      kv_cache[slot * ORC_D_QK + c] = orc_fp8_encode((double)scaled);
+    }
+  }
+}
+
+/* ---------------------------------------------------------- split bounds */
+
+static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+/* Split-KV partition.  [MLA] `m1c_inputs` gives only the shape of the
+ * partials, o [splits, S, H, 512] and LSE [splits, S, H].  Reading taken:
+ * the concatenated KV token stream (the order of kv_indices) is cut every
+ * `chunk` tokens, with
+ *   chunk = max(split_min_tokens, ceil(T / num_workers),
+ *               ceil(L_max / (num_splits - 1)))   (num_splits > 1)
+ *   chunk = max(1, T)                              (num_splits == 1)
+ * where T is the total number of tokens and L_max the longest request.  A
+ * request's splits are its pieces between consecutive cuts, in order; the
+ * third term keeps every request within num_splits pieces.  bounds[r][k] is
+ * the first token (within request r) of split k; bounds[r][num_splits] =
+ * L_r and unused splits are empty (bounds equal to L_r).
+ * Returns chunk. */
+int64_t orc_split_bounds(const int32_t* indptr, int32_t batch, int32_t num_splits,
+                         int32_t num_workers, int32_t split_min_tokens, int32_t* bounds) {
+  int64_t T = (int64_t)indptr[batch] - indptr[0];
+  int64_t lmax = 0;
+  for (int32_t r = 0; r < batch; ++r) {
+    int64_t L = (int64_t)indptr[r + 1] - indptr[r];
+    if (L > lmax) lmax = L;
+  }
+  int64_t chunk = split_min_tokens > 1 ? split_min_tokens : 1;
+  if (num_splits > 1) {
+    int64_t a = num_workers > 0 ? ceil_div64(T, num_workers) : T;
+    int64_t b = ceil_div64(lmax, num_splits - 1);
+    if (a > chunk) chunk = a;
+    if (b > chunk) chunk = b;
+  } else {
+    if (T > chunk) chunk = T;
+  }
+  for (int32_t r = 0; r < batch; ++r) {
+    int64_t P = (int64_t)indptr[r] - indptr[0];
+    int64_t L = (int64_t)indptr[r + 1] - indptr[r];
+    int32_t* b = bounds + (int64_t)r * (num_splits + 1);
+    int k = 0;
+    b[k++] = 0;
+    /* every multiple of chunk strictly inside (P, P + L) starts a split */
+    for (int64_t c = (P / chunk + 1) * chunk; c < P + L; c += chunk) b[k++] = (int32_t)(c - P);
+    while (k <= num_splits) b[k++] = (int32_t)L;
+  }
+  return chunk;
+}
+
+/* ----------------------------------------------------- attention (exact) */
+
+/* Exact softmax attention of one query row of one head over tokens
+ * [lo, hi) of request r (definition behind [MLA] `attend` / `m1c_inputs`):
+ *   s_i = sm_scale * kv_scale * sum_{d<576} q[d] * D(kv[row_i][d])
+ *   LSE = ln sum_i exp(s_i),   o = kv_scale * sum_i exp(s_i - LSE) * D(kv[row_i][0:512])
+ * An empty range gives LSE = -inf and o = 0. */
+static void attend_row(const uint16_t* qrow, const uint8_t* kv_cache, const int32_t* rows,
+                       int64_t lo, int64_t hi, double sm_scale, double kv_scale, double* s,
+                       double* lse_out, double* o_out) {
+  for (int d = 0; d < ORC_D_LATENT; ++d) o_out[d] = 0.0;
+  if (hi <= lo) {
+    *lse_out = -INFINITY;
+    return;
+  }
+  double qd[ORC_D_QK];
+  for (int d = 0; d < ORC_D_QK; ++d) qd[d] = orc_bf16_decode(qrow[d]);
+  double m = -INFINITY;
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint8_t* kr = kv_cache + (int64_t)rows[i] * ORC_D_QK;
+    double dot = 0.0;
+    for (int d = 0; d < ORC_D_QK; ++d) dot += qd[d] * orc_fp8_decode(kr[d]);
+    s[i - lo] = sm_scale * kv_scale * dot;
+    if (s[i - lo] > m) m = s[i - lo];
+  }
+  double sum = 0.0;
+  for (int64_t i = lo; i < hi; ++i) sum += exp(s[i - lo] - m);
+  double lse = m + log(sum);
+  for (int64_t i = lo; i < hi; ++i) {
+    const uint8_t* kr = kv_cache + (int64_t)rows[i] * ORC_D_QK;
+    double p = exp(s[i - lo] - lse);
+    for (int d = 0; d < ORC_D_LATENT; ++d) o_out[d] += p * orc_fp8_decode(kr[d]);
+  }
+  for (int d = 0; d < ORC_D_LATENT; ++d) o_out[d] *= kv_scale;
+  *lse_out = lse;
+}
+
+/* Split-KV partial attention ([MLA] `m1c_inputs`: o [splits, S, H, 512]
+ * and LSE [splits, S, H]).  q is [S, H, 576] contiguous with S = batch*qlen;
+ * row t = r*qlen + j belongs to request r.  Reading taken for qlen > 1 (the
+ * pages run qlen 4 / 8 without stating the mask): the cache already holds
+ * the request's qlen new tokens, and row j sees the first
+ * L_r - qlen + j + 1 tokens (causal within the window).  Split k of row t is
+ * the exact attention over [bounds[r][k], bounds[r][k+1]) intersected with
+ * the visible prefix; o_out / lse_out are [num_splits][S][H][512] / [..][H]
+ * in double (rounding o to bf16 is a separate step). */
+void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t heads,
+                        const uint8_t* kv_cache, const int32_t* indptr, const int32_t* indices,
+                        const int32_t* bounds, int32_t num_splits, double sm_scale,
+                        double kv_scale, double* o_out, double* lse_out) {
+  int64_t S = (int64_t)batch * qlen;
+  int64_t lmax = 0;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr[r + 1] - indptr[r] > lmax) lmax = indptr[r + 1] - indptr[r];
+  int64_t total = (int64_t)num_splits * S * heads;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)(lmax > 0 ? lmax : 1));
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t w = 0; w < total; ++w) {
+      int64_t h = w % heads;
+      int64_t t = (w / heads) % S;
+      int64_t k = w / (heads * S);
+      int64_t r = t / qlen, j = t % qlen;
+      int64_t L = (int64_t)indptr[r + 1] - indptr[r];
+      int64_t visible = L - qlen + j + 1;
+      if (visible < 0) visible = 0;
+      const int32_t* b = bounds + r * (num_splits + 1);
+      int64_t lo = b[k], hi = b[k + 1];
+      if (hi > visible) hi = visible;
+      const int32_t* rows = indices + indptr[r];
+      attend_row(q + (t * heads + h) * ORC_D_QK, kv_cache, rows, lo, hi, sm_scale, kv_scale, s,
+                 lse_out + (k * S + t) * heads + h, o_out + ((k * S + t) * heads + h) * ORC_D_LATENT);
+    }
+    free(s);
+  }
+}
+
+/* -------------------------------------------------------------- merge */
+
+/* LSE merge of split partials ([MLA] `m1c_inputs`: "M1b merges the splits";
+ * the same combine `post` applies across ranks).  For each (row, head):
+ *   m = max_k LSE_k; if m = -inf: o = 0, LSE = -inf; otherwise
+ *   LSE = m + ln sum_k exp(LSE_k - m),  o = sum_k exp(LSE_k - LSE) * o_k
+ * where o_k is the stored bf16 partial.  Splits with LSE_k = -inf contribute
+ * nothing and their o_k is never read (it may hold anything).
+ * o_part [num_splits][rows][heads][512] bf16, lse_part [num_splits][rows][heads]. */
+void orc_merge_lse(const uint16_t* o_part, const float* lse_part, int32_t num_splits, int64_t rows,
+                   int32_t heads, double* o_out, double* lse_out) {
+  int64_t n = rows * heads;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    double m = -INFINITY;
+    for (int k = 0; k < num_splits; ++k) {
+      double l = lse_part[k * n + i];
+      if (l > m) m = l;
+    }
+    double* o = o_out + i * ORC_D_LATENT;
+    for (int d = 0; d < ORC_D_LATENT; ++d) o[d] = 0.0;
+    if (m == -INFINITY) {
+      lse_out[i] = -INFINITY;
+      continue;
+    }
+    double sum = 0.0;
+    for (int k = 0; k < num_splits; ++k) {
+      double l = lse_part[k * n + i];
+      if (l != -INFINITY) sum += exp(l - m);
+    }
+    double lse = m + log(sum);
+    for (int k = 0; k < num_splits; ++k) {
+      double l = lse_part[k * n + i];
+      if (l == -INFINITY) continue;
+      double wgt = exp(l - lse);
+      const uint16_t* ok = o_part + (k * n + i) * ORC_D_LATENT;
+      for (int d = 0; d < ORC_D_LATENT; ++d) o[d] += wgt * orc_bf16_decode(ok[d]);
+    }
+    lse_out[i] = lse;
+  }
+}
+
+/* ------------------------------------------------------- value + gate */
+
+/* W_UV value projection and sigmoid gate ([VALUE] `MlaValue`, `MlaGate`;
+ * [MLA] `post`).  For row t (request t / qlen), head h, output v < 128:
+ *   acc = sum_{l<512} latent[t][h][l] * W(h, v, l)
+ *   out[t][h*128 + v] = bf16( f32(bf16(acc)) * sigmoid(f32(gate[t][h*128+v])) )
+ * when lengths[t / qlen] > 0, and +0 otherwise (even for a NaN gate or a
+ * NaN latent).  W is bf16 [H][128][512] (latent axis contiguous), or, when
+ * w_fp4 != NULL, MXFP4: codes [H][128][256] bytes (element 2k in the low
+ * nibble) with E8M0 scales [H][128][16], one per 32 consecutive latents.
+ * acc_out (may be NULL) receives acc in double; out receives bf16 bits. */
+void orc_value_gate(const uint16_t* latent, const uint16_t* w_bf16, const uint8_t* w_fp4,
+                    const uint8_t* w_scale, const uint16_t* gate, const int32_t* lengths,
+                    int32_t batch, int32_t qlen, int32_t heads, double* acc_out, uint16_t* out) {
+  int64_t S = (int64_t)batch * qlen;
+  int64_t n = S * heads;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t t = i / heads, h = i % heads;
+    int64_t r = t / qlen;
+    const uint16_t* lat = latent + i * ORC_D_LATENT;
+    for (int v = 0; v < ORC_D_V; ++v) {
+      double acc = 0.0;
+      for (int l = 0; l < ORC_D_LATENT; ++l) {
+        double w;
+        if (w_fp4) {
+          uint8_t byte = w_fp4[((h * ORC_D_V + v) * ORC_D_LATENT + l) / 2];
+          uint8_t nib = (l & 1) ? (byte >> 4) : (byte & 0xF);
+          w = orc_e2m1_decode(nib) * orc_e8m0_decode(w_scale[(h * ORC_D_V + v) * 16 + l / 32]);
+        } else {
+          w = orc_bf16_decode(w_bf16[(h * ORC_D_V + v) * ORC_D_LATENT + l]);
+        }
+        acc += orc_bf16_decode(lat[l]) * w;
+      }
+      int64_t col = h * ORC_D_V + v;
+      if (acc_out) acc_out[t * heads * ORC_D_V + col] = acc;
+      if (lengths[r] > 0) {
+        double value = orc_bf16_decode(orc_bf16_round(acc));
+        float g = (float)orc_bf16_decode(gate[t * heads * ORC_D_V + col]);
+        double sig = 1.0 / (1.0 + exp(-(double)g));
+        out[t * heads * ORC_D_V + col] = orc_bf16_round(value * sig);
+      } else {
+        out[t * heads * ORC_D_V + col] = 0; /* +0 */
+      }
+    }
+  }
+}
+
+/* elementwise array forms of the codecs above */
+void orc_bf16_round_array(const double* in, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_bf16_round(in[i]);
+}
+void orc_fp8_encode_array(const double* in, uint8_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_fp8_encode(in[i]);
+}
+
+/* number of OpenMP threads the oracle runs on (for reporting) */
+int orc_num_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

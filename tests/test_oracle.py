@@ -1,0 +1,457 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against a closed form, a library routine that
+computes the same definition (torch's fp8 / e8m0 / bf16 casts, torch's
+scaled-dot-product attention and logsumexp, numpy matmul, scipy's expit),
+brute force on tiny inputs, or an invariant of the method.  The pages print
+no worked example (tests/golden/README.md), so no pin quotes a printed value.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+from mla_latent_kv_fp8_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ------------------------------------------------------------------ codecs
+
+def test_fp8_decode_matches_torch_e4m3fn(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.fp8_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.array_equal(np.signbit(ours[ok]), np.signbit(ref[ok]))
+
+
+def test_fp8_named_points_from_spec(oracle):
+    for line in open(os.path.join(GOLDEN, "ocp_fp8_e4m3.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = oracle.fp8_decode(np.array([int(code, 16)], dtype=np.uint8))[0]
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val))
+
+
+def test_fp8_encode_roundtrip_all_finite_codes(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.fp8_decode(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(oracle.fp8_encode(vals[fin]), codes[fin])
+
+
+def _nearest_even_bruteforce(v, table_vals, table_codes):
+    """Nearest finite fp8 value, ties to the even code, saturating: brute
+    force over the finite positive codes."""
+    a = abs(v)
+    if a >= 448:
+        c = 0x7E
+    else:
+        d = np.abs(table_vals - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(table_codes[best[0]]) if len(best) == 1 else int(
+            [table_codes[i] for i in best if table_codes[i] % 2 == 0][0])
+    return c | (0x80 if np.signbit(v) else 0)
+
+
+def test_fp8_encode_bruteforce_midpoints_and_saturation(oracle):
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    pv = oracle.fp8_decode(pos)
+    mids = (pv[:-1] + pv[1:]) / 2.0
+    rng = np.random.default_rng(0)
+    probes = np.concatenate([mids, -mids, pv * 1.0001, pv * 0.9999, rng.uniform(-500, 500, 2000),
+                             [449.0, 464.0, 465.0, 1e6, -1e6, 0.0, -0.0, 1e-30]])
+    got = oracle.fp8_encode(probes)
+    want = np.array([_nearest_even_bruteforce(v, pv, pos) for v in probes], dtype=np.uint8)
+    assert np.array_equal(got, want)
+    assert oracle.fp8_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_fp8_encode_matches_torch_cast_in_range(oracle):
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000) * 30, rng.uniform(-448, 448, 20000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.fp8_encode(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_matches_torch_for_binary32_inputs(oracle):
+    rng = np.random.default_rng(2)
+    bits = rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    # ties: low 16 bits exactly 0x8000
+    ties = ((rng.integers(0, 2**16, 5000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties[np.isfinite(ties)]])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_round(x.astype(np.float64)), ref)
+
+
+def test_bf16_round_direct_not_double_rounded(oracle):
+    # 1 + 2^-8 + 2^-30 lies just above a bf16 tie: direct rounding goes up,
+    # rounding through binary32 first would land on the tie and go to even.
+    x = 1.0 + 2.0**-8 + 2.0**-30
+    assert oracle.bf16_decode(oracle.bf16_round(np.array([x])))[0] == 1.0 + 2.0**-7
+    assert oracle.bf16_round(np.array([np.nan]))[0] == 0x7FC0
+
+
+def test_e2m1_table_from_spec(oracle):
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "ocp_mx_e2m1.txt")) if l.strip() and l[0] != "#"]
+    for code, val in rows:
+        c = int(code)
+        assert oracle.e2m1_decode(np.array([c]))[0] == float(val)
+        neg = oracle.e2m1_decode(np.array([c | 8]))[0]
+        assert neg == -float(val) and np.signbit(neg)
+
+
+def test_e8m0_matches_torch(oracle):
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e8m0_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255])
+
+
+# ------------------------------------------------------------- kv write
+
+def test_kv_write_bruteforce_and_skip(oracle):
+    rng = np.random.default_rng(3)
+    n, slots, kv_scale = 7, 13, 0.05
+    rows = synth.to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32) * 0.5)
+    slot_map = np.array([3, 0, -1, 12, 7, 5, 9], dtype=np.int64)
+    cache = np.full((slots, 576), 0x7F, dtype=np.uint8)
+    out = oracle.kv_write(rows[:, :512], rows[:, 512:], slot_map, cache, kv_scale)
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    pv = oracle.fp8_decode(pos)
+    for i, s in enumerate(slot_map):
+        if s < 0:
+            continue
+        x = oracle.bf16_decode(rows[i]).astype(np.float32)
+        scaled = (x / np.float32(kv_scale)).astype(np.float64)  # binary32 division
+        want = [_nearest_even_bruteforce(v, pv, pos) for v in scaled]
+        assert np.array_equal(out[s], np.array(want, dtype=np.uint8))
+    untouched = sorted(set(range(slots)) - set(int(s) for s in slot_map if s >= 0))
+    assert (out[untouched] == 0x7F).all()
+
+
+# ---------------------------------------------------------- split bounds
+
+def test_split_bounds_tiny_worked_example(oracle):
+    indptr = np.array([0, 37, 101], dtype=np.int32)
+    b, chunk = oracle.split_bounds(indptr, 2, 256, 1)
+    lines = [l for l in open(os.path.join(GOLDEN, "split_bounds_tiny.txt")) if l[0] != "#"]
+    want = np.array([[int(v) for v in l.split(":")[1].split()] for l in lines], dtype=np.int32)
+    assert chunk == 64
+    assert np.array_equal(b, want)
+
+
+@pytest.mark.parametrize("lens,ns,W,mn", [
+    ([1024, 8192, 0, 4000, 17], 16, 256, 256),
+    ([5, 0, 0, 9], 3, 4, 1),
+    ([100000, 3, 64000], 64, 256, 256),
+    ([10, 20, 30], 1, 256, 1),
+    ([0, 0], 4, 8, 1),
+])
+def test_split_bounds_properties(oracle, lens, ns, W, mn):
+    lens = np.array(lens)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    b, chunk = oracle.split_bounds(indptr, ns, W, mn)
+    T = int(lens.sum())
+    assert chunk >= max(1, mn)
+    for r, L in enumerate(lens):
+        br = b[r]
+        assert br[0] == 0 and br[-1] == L and (np.diff(br) >= 0).all()
+        P = int(indptr[r])
+        for k in range(ns):
+            lo, hi = int(br[k]), int(br[k + 1])
+            if hi > lo:
+                # a piece never crosses a multiple of chunk in stream coordinates
+                assert (P + lo) // chunk == (P + hi - 1) // chunk
+                if k > 0:
+                    assert (P + lo) % chunk == 0
+        # pieces are maximal: consecutive non-empty pieces sit in consecutive chunks
+        if L > 0:
+            n_pieces = (P + L - 1) // chunk - P // chunk + 1
+            assert n_pieces <= ns
+            assert int((np.diff(br) > 0).sum()) == n_pieces
+
+
+# ------------------------------------------------------------- attention
+
+def _decode_kv(kv):
+    return torch.from_numpy(np.ascontiguousarray(kv)).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def _bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+
+
+def _sdpa_reference(q_bits, kv_bytes, indptr, indices, qlen, sm_scale, kv_scale):
+    """Library attention: torch SDPA (float64, CPU) with a boolean causal
+    window mask, and torch.logsumexp for the LSE."""
+    S, H, _ = q_bits.shape
+    B = len(indptr) - 1
+    o = np.zeros((S, H, 512))
+    lse = np.full((S, H), -np.inf)
+    for r in range(B):
+        L = int(indptr[r + 1] - indptr[r])
+        if L == 0:
+            continue
+        rows = indices[indptr[r]:indptr[r + 1]]
+        kv = _decode_kv(kv_bytes[rows])           # [L, 576]
+        q = _bf16(q_bits[r * qlen:(r + 1) * qlen])  # [qlen, H, 576]
+        vis = torch.tensor([[i < L - qlen + j + 1 for i in range(L)] for j in range(qlen)])
+        qq = q.permute(1, 0, 2).unsqueeze(0)       # [1, H, qlen, 576]
+        k = kv.unsqueeze(0).unsqueeze(0)           # [1, 1, L, 576]
+        v = kv[:, :512].unsqueeze(0).unsqueeze(0) * kv_scale
+        scale = sm_scale * kv_scale
+        out = torch.nn.functional.scaled_dot_product_attention(
+            qq, k.expand(1, H, L, 576), v.expand(1, H, L, 512), attn_mask=vis, scale=scale)
+        scores = torch.matmul(qq, k.expand(1, H, L, 576).transpose(-1, -2)) * scale
+        scores = scores.masked_fill(~vis, -math.inf)
+        l = torch.logsumexp(scores, dim=-1)        # [1, H, qlen]
+        o[r * qlen:(r + 1) * qlen] = out[0].permute(1, 0, 2).numpy()
+        lse[r * qlen:(r + 1) * qlen] = l[0].permute(1, 0).numpy()
+    return o, lse
+
+
+def _tiny_problem(rng, lens, H, qlen, kv_scale=1.0, std=0.5):
+    lens = np.array(lens)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(lens.sum())
+    nslots = max(1, int(T * 1.25) + 3)
+    indices = rng.permutation(nslots)[:T].astype(np.int32)
+    kv = np.full((nslots, 576), 0x7F, dtype=np.uint8)  # unused rows are NaN
+    xs = synth.to_bf16_bits(rng.standard_normal((T, 576)).astype(np.float32) * std)
+    scaled = _bf16(xs).to(torch.float32) / kv_scale   # library fp8 cast makes the test cache
+    kv[indices] = scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q = synth.to_bf16_bits(rng.standard_normal((len(lens) * qlen, H, 576)).astype(np.float32))
+    return q, kv, indptr, indices
+
+
+@pytest.mark.parametrize("lens,H,qlen,kv_scale", [
+    ([37, 64], 16, 1, 1.0),
+    ([5, 1, 0, 33], 3, 1, 0.05),
+    ([9, 16, 4], 2, 4, 0.05),
+    ([20, 8], 4, 8, 0.5),
+])
+def test_attention_matches_library_sdpa(oracle, lens, H, qlen, kv_scale):
+    rng = np.random.default_rng(len(lens) * 100 + H)
+    q, kv, indptr, indices = _tiny_problem(rng, lens, H, qlen, kv_scale)
+    sm = 1 / math.sqrt(192)
+    b, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, b, qlen, sm, kv_scale)
+    ro, rl = _sdpa_reference(q, kv, indptr, indices, qlen, sm, kv_scale)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse[0]), fin)
+    np.testing.assert_allclose(lse[0][fin], rl[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0][fin], ro[fin], rtol=0, atol=1e-12)
+    assert (o[0][~fin] == 0).all()
+
+
+def test_attention_closed_forms(oracle):
+    rng = np.random.default_rng(7)
+    sm, kv_scale = 0.1, 0.25
+    # L = 1: o = kv_scale * v0, LSE = s0
+    q, kv, indptr, indices = _tiny_problem(rng, [1], 4, 1, kv_scale)
+    b, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, b, 1, sm, kv_scale)
+    row = oracle.fp8_decode(kv[indices[0]])
+    qd = oracle.bf16_decode(q[0])
+    np.testing.assert_allclose(o[0, 0], kv_scale * row[None, :512].repeat(4, 0), atol=1e-15)
+    np.testing.assert_allclose(lse[0, 0], sm * kv_scale * (qd @ row), atol=1e-12)
+    # q = 0: uniform weights, o = kv_scale * mean(v), LSE = ln n
+    q, kv, indptr, indices = _tiny_problem(rng, [11], 2, 1, kv_scale)
+    q[:] = 0
+    b, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, b, 1, sm, kv_scale)
+    v = oracle.fp8_decode(kv[indices])[:, :512]
+    np.testing.assert_allclose(o[0, 0, 0], kv_scale * v.mean(0), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], np.log(11), atol=1e-14)
+    # identical keys on the scored dims: q zero on the latent, rows sharing
+    # their rope bytes -> equal scores -> o = mean of the latents, LSE = s + ln n
+    q, kv, indptr, indices = _tiny_problem(rng, [9], 3, 1, kv_scale)
+    q[:, :, :512] = 0
+    kv[indices, 512:] = kv[indices[0], 512:]
+    b, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, b, 1, sm, kv_scale)
+    v = oracle.fp8_decode(kv[indices])
+    s0 = sm * kv_scale * (oracle.bf16_decode(q[0]) @ v[0])
+    np.testing.assert_allclose(o[0, 0], kv_scale * v[:, :512].mean(0)[None].repeat(3, 0), atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], s0 + np.log(9), atol=1e-12)
+    # empty request: LSE = -inf and o = 0
+    q, kv, indptr, indices = _tiny_problem(rng, [0, 3], 2, 1, kv_scale)
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, oracle.split_bounds(indptr, 1, 1, 1)[0], 1, sm,
+                                   kv_scale)
+    assert np.isneginf(lse[0, 0]).all() and (o[0, 0] == 0).all() and np.isfinite(lse[0, 1]).all()
+
+
+def test_causal_window_rows_see_prefix(oracle):
+    # row j of a qlen window equals a qlen=1 query over the first L-qlen+j+1 tokens
+    rng = np.random.default_rng(8)
+    qlen, L, H = 4, 10, 2
+    q, kv, indptr, indices = _tiny_problem(rng, [L], H, qlen)
+    sm = 0.07
+    o, lse = oracle.decode_partial(q, kv, indptr, indices, oracle.split_bounds(indptr, 1, 1, 1)[0], qlen,
+                                   sm, 1.0)
+    for j in range(qlen):
+        n = L - qlen + j + 1
+        ip = np.array([0, n], dtype=np.int32)
+        o1, l1 = oracle.decode_partial(q[j:j + 1], kv, ip, indices[:n], oracle.split_bounds(ip, 1, 1, 1)[0],
+                                       1, sm, 1.0)
+        np.testing.assert_array_equal(o1[0, 0], o[0, j])
+        np.testing.assert_array_equal(l1[0, 0], lse[0, j])
+
+
+def _merge_f64(o, lse):
+    """merge in double of unrounded partials (an invariant check, not a pin
+    of the bf16 merge)."""
+    lse = np.asarray(lse, dtype=np.float64)
+    m = lse.max(0)
+    out = np.zeros(o.shape[1:])
+    tot = np.full(lse.shape[1:], -np.inf)
+    fin = np.isfinite(m)
+    w = np.where(np.isfinite(lse), np.exp(lse - np.where(fin, m, 0)[None]), 0.0)
+    ssum = w.sum(0)
+    tot[fin] = m[fin] + np.log(ssum[fin])
+    out[fin] = (w[:, fin, None] * o[:, fin]).sum(0) / ssum[fin, None]
+    return out, tot
+
+
+@pytest.mark.parametrize("ns,W,mn", [(2, 256, 1), (4, 8, 3), (7, 16, 2)])
+def test_split_partials_merge_to_unsplit(oracle, ns, W, mn):
+    rng = np.random.default_rng(9 + ns)
+    lens, H, qlen = [37, 64, 0, 19], 3, 2
+    q, kv, indptr, indices = _tiny_problem(rng, lens, H, qlen, 0.05)
+    sm = 1 / math.sqrt(192)
+    b1, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o1, l1 = oracle.decode_partial(q, kv, indptr, indices, b1, qlen, sm, 0.05)
+    b, chunk = oracle.split_bounds(indptr, ns, W, mn)
+    assert (np.diff(b, axis=1) > 0).sum(1).max() > 1  # some request really is split
+    o, l = oracle.decode_partial(q, kv, indptr, indices, b, qlen, sm, 0.05)
+    om, lm = _merge_f64(o, l)
+    np.testing.assert_allclose(lm[np.isfinite(lm)], l1[0][np.isfinite(lm)], atol=1e-12)
+    assert np.array_equal(np.isfinite(lm), np.isfinite(l1[0]))
+    np.testing.assert_allclose(om, o1[0], atol=1e-13)
+
+
+def test_page_table_permutation_invariance(oracle):
+    rng = np.random.default_rng(10)
+    q, kv, indptr, indices = _tiny_problem(rng, [23, 40], 4, 1)
+    b, _ = oracle.split_bounds(indptr, 3, 4, 1)
+    o, l = oracle.decode_partial(q, kv, indptr, indices, b, 1, 0.08, 1.0)
+    perm = rng.permutation(kv.shape[0])      # move every row ...
+    kv2 = np.empty_like(kv)
+    kv2[perm] = kv
+    idx2 = perm[indices].astype(np.int32)    # ... and its index with it
+    o2, l2 = oracle.decode_partial(q, kv2, indptr, idx2, b, 1, 0.08, 1.0)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+
+
+# ------------------------------------------------------------------ merge
+
+def test_merge_single_split_passes_through(oracle):
+    rng = np.random.default_rng(11)
+    o, l = synth.random_partials(rng, 1, 5, 3, p_empty=0.2)
+    mo, ml = oracle.merge_lse(o, l)
+    fin = np.isfinite(l[0])
+    np.testing.assert_array_equal(oracle.bf16_round(mo[fin]), o[0][fin])
+    np.testing.assert_array_equal(ml[fin], l[0][fin].astype(np.float64))
+    assert (mo[~fin] == 0).all() and np.isneginf(ml[~fin]).all()
+
+
+def test_merge_two_splits_closed_form(oracle):
+    # equal LSEs: o = mean, LSE = lse + ln 2; a -inf split is ignored (NaN o)
+    o = np.zeros((3, 1, 1, 512), dtype=np.uint16)
+    a = synth.to_bf16_bits(np.linspace(-1, 1, 512).astype(np.float32))
+    bb = synth.to_bf16_bits(np.linspace(2, -3, 512).astype(np.float32))
+    o[0, 0, 0], o[1, 0, 0], o[2, 0, 0] = a, bb, synth.BF16_NAN
+    lse = np.array([0.5, 0.5, -np.inf], dtype=np.float32).reshape(3, 1, 1)
+    mo, ml = oracle.merge_lse(o, lse)
+    np.testing.assert_allclose(mo[0, 0], (oracle.bf16_decode(a) + oracle.bf16_decode(bb)) / 2, atol=1e-15)
+    np.testing.assert_allclose(ml[0, 0], 0.5 + np.log(2), atol=1e-15)
+    # unequal: weights e^{l_k} / sum
+    lse = np.array([0.0, math.log(3.0), -np.inf], dtype=np.float32).reshape(3, 1, 1)
+    mo, ml = oracle.merge_lse(o, lse)
+    e1 = math.exp(float(np.float32(math.log(3.0))))
+    np.testing.assert_allclose(mo[0, 0], (oracle.bf16_decode(a) + e1 * oracle.bf16_decode(bb)) / (1 + e1),
+                               atol=1e-14)
+    np.testing.assert_allclose(ml[0, 0], math.log(1 + e1), atol=1e-14)
+
+
+def test_merge_all_empty_and_associativity(oracle):
+    rng = np.random.default_rng(12)
+    o, l = synth.random_partials(rng, 4, 6, 2, p_empty=0.3)
+    l[:, 0, 0] = -np.inf
+    mo, ml = oracle.merge_lse(o, l)
+    assert (mo[0, 0] == 0).all() and np.isneginf(ml[0, 0])
+    assert not np.isnan(mo).any()
+    # merging (0,1) and (2,3) separately in double, then merging the results
+    # in double, equals merging all four
+    f = lambda oo, ll: _merge_f64(np.where(np.isfinite(ll)[..., None], oracle.bf16_decode(oo), 0.0), ll)
+    a_o, a_l = f(o[:2], l[:2])
+    b_o, b_l = f(o[2:], l[2:])
+    c_o, c_l = _merge_f64(np.stack([a_o, b_o]), np.stack([a_l, b_l]))
+    fin = np.isfinite(ml)
+    np.testing.assert_allclose(c_o[fin], mo[fin], atol=1e-13)
+    np.testing.assert_allclose(c_l[fin], ml[fin], atol=1e-13)
+
+
+# ----------------------------------------------------------- value + gate
+
+def test_value_bf16_matches_numpy_matmul_and_gate(oracle):
+    w = synth.make("tiny")
+    rng = np.random.default_rng(13)
+    S, H = w.S, w.heads
+    lat = synth.to_bf16_bits(rng.standard_normal((S, H, 512)).astype(np.float32) * 0.3)
+    acc, out = oracle.value_gate(lat, w.gate, w.lengths, w.qlen, w_bf16=w.w_uv)
+    L = oracle.bf16_decode(lat)
+    W = oracle.bf16_decode(w.w_uv)                         # [H, 128, 512]
+    ref = np.einsum("shl,hvl->shv", L, W).reshape(S, H * 128)  # numpy contraction in double
+    np.testing.assert_allclose(acc, ref, rtol=1e-12, atol=1e-12)
+    g = oracle.bf16_decode(w.gate).astype(np.float32).astype(np.float64)
+    val = oracle.bf16_decode(oracle.bf16_round(ref))
+    want = oracle.bf16_round(val * expit(g))
+    assert np.array_equal(out, want)
+
+
+def test_value_mxfp4_matches_table_expansion(oracle):
+    w = synth.make("rank_share", batch=2, len_range=(5, 9))
+    rng = np.random.default_rng(14)
+    S, H = w.S, w.value_heads
+    lat = synth.to_bf16_bits(rng.standard_normal((S, H, 512)).astype(np.float32) * 0.3)
+    acc, _ = oracle.value_gate(lat, w.gate, w.lengths, w.qlen, w_fp4=w.w_fp4, w_scale=w.w_scale)
+    table = {int(l.split()[0]): float(l.split()[1]) for l in open(os.path.join(GOLDEN, "ocp_mx_e2m1.txt"))
+             if l[0] != "#" and l.strip()}
+    mag = np.array([table[c & 7] for c in range(16)]) * np.where(np.arange(16) >= 8, -1, 1)
+    codes = np.stack([w.w_fp4 & 0xF, w.w_fp4 >> 4], -1).reshape(H, 128, 512)
+    scale = 2.0 ** (w.w_scale.astype(np.float64) - 127)
+    W = mag[codes] * np.repeat(scale, 32, axis=-1)
+    ref = np.einsum("shl,hvl->shv", oracle.bf16_decode(lat), W).reshape(S, H * 128)
+    np.testing.assert_allclose(acc, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gate_closed_forms_and_empty_rows(oracle):
+    rng = np.random.default_rng(15)
+    B, qlen, H = 3, 2, 2
+    lengths = np.array([4, 0, 1], dtype=np.int32)
+    lat = synth.to_bf16_bits(rng.standard_normal((B * qlen, H, 512)).astype(np.float32))
+    wuv = synth.to_bf16_bits(rng.standard_normal((H, 128, 512)).astype(np.float32) * 0.05)
+    gate = np.zeros((B * qlen, H * 128), dtype=np.uint16)  # logit +0 -> sigmoid 1/2 exactly
+    gate[2:4] = synth.BF16_NAN                             # empty request's rows
+    lat[2:4] = synth.BF16_NAN
+    acc, out = oracle.value_gate(lat, gate, lengths, qlen, w_bf16=wuv)
+    keep = np.ones(B * qlen, bool)
+    keep[2:4] = False
+    half = oracle.bf16_decode(oracle.bf16_round(acc[keep])) / 2   # exact halving
+    assert np.array_equal(oracle.bf16_decode(out[keep]), half)
+    assert (out[~keep] == 0).all()                                  # +0 bits
