@@ -1,0 +1,196 @@
+"""Benchmark of the MLA fp8-KV decode step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input already
+resident in HBM: kv_write (the step's new tokens) -> decode_partial ->
+merge_lse -> value_gate.  Default workload: the batch-decode configuration
+(64 requests, qlen 1, 96 heads in a 128-head query buffer, fp8 KV with
+kv_scale 0.05, context lengths uniform in [1024, 8192], 4 empty requests,
+bf16 W_UV).
+
+Each timed step is preceded (outside its HIP events) by a 512 MiB write
+that evicts the KV cache from L2 and the Infinity Cache, so `value` is a
+cold-cache, HBM-served figure; warm back-to-back numbers are reported
+alongside.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="batch")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def algorithmic(w):
+    """KV bytes and MFMA flops of the partial kernel per launch."""
+    L = w.lengths.astype(np.int64)
+    kv_bytes = int(L.sum()) * 576
+    visible = 0
+    for j in range(w.qlen):
+        visible += int(np.maximum(L - w.qlen + j + 1, 0)[L > 0].sum())
+    flops = 2176 * w.heads * visible
+    return kv_bytes, flops
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    the first requests of the batch until about `budget_s` of CPU work."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import oracle
+
+    oracle.lib()
+    H = w.heads
+    nonempty = [r for r in range(w.batch) if w.lengths[r] > 0]
+    done_bytes, t_total, n_req = 0, 0.0, 0
+    for r in nonempty:
+        L = int(w.lengths[r])
+        rows = w.indices[w.indptr[r]:w.indptr[r + 1]]
+        x = w.kv_rows[w.indptr[r]:w.indptr[r + 1]]
+        t0 = time.perf_counter()
+        cache = oracle.kv_write(x[:, :512], x[:, 512:], np.arange(L, dtype=np.int64),
+                                np.zeros((L, 576), np.uint8), w.kv_scale)
+        ip = np.array([0, L], np.int32)
+        b, _ = oracle.split_bounds(ip, 1, 1, 1)
+        q = np.ascontiguousarray(w.q[r * w.qlen:(r + 1) * w.qlen, :H])
+        o, l = oracle.decode_partial(q, cache, ip, np.arange(L, dtype=np.int32), b, w.qlen, w.sm_scale,
+                                     w.kv_scale)
+        lat = oracle.bf16_round(o[0])
+        oracle.value_gate(lat, w.gate[r * w.qlen:(r + 1) * w.qlen, :H * 128], w.lengths[r:r + 1], w.qlen,
+                          w_bf16=None if w.w_uv is None else w.w_uv[:H],
+                          w_fp4=None if w.w_fp4 is None else w.w_fp4[:H],
+                          w_scale=None if w.w_scale is None else w.w_scale[:H])
+        t_total += time.perf_counter() - t0
+        done_bytes += L * 576
+        n_req += 1
+        if t_total >= budget_s:
+            break
+    return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "%d of %d requests of the workload (all %d heads, whole contexts, %d KV tokens): "
+                      "cache write + exact attention + W_UV/gate, %.1f s" %
+                      (n_req, w.batch, H, done_bytes // 576, t_total)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mla_latent_kv_fp8_amd as m
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    m.lib()
+    w = synth.make(args.config)
+    print("[bench] workload %s: B=%d qlen=%d H=%d tokens=%d" % (w.name, w.batch, w.qlen, w.heads, w.total_tokens),
+          file=sys.stderr, flush=True)
+    st = DeviceStep(w)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    for i in range(K):
+        flush.zero_()  # evict L2 / Infinity Cache (outside the step's events)
+        ev[i][0].record()
+        st.write_new_tokens()
+        st.attend()
+        ev[i][1].record()
+        st.merge()
+        st.value()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    attn_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    # warm: the same steps back to back
+    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wa.record()
+    for _ in range(K):
+        st.run()
+    wb.record()
+    torch.cuda.synchronize()
+    warm_ms = wa.elapsed_time(wb) / K
+
+    # the partial kernel alone (its own events), cold
+    pk = []
+    for _ in range(K):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        st.attend()
+        b.record()
+        pk.append((a, b))
+    torch.cuda.synchronize()
+    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in pk]))
+
+    kv_bytes, flops = algorithmic(w)
+    ms = float(np.mean(step_ms))
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    tflops = flops / (partial_ms * 1e-3) / 1e12
+    gbs_partial = kv_bytes / (partial_ms * 1e-3) / 1e9
+    out = {
+        "metric": "MLA decode: fp8-KV GB/s + MFMA TFLOP/s vs peak; us/step at B=64, H=128",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "us_per_step_warm": round(warm_ms * 1e3, 2),
+        "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 KV, bf16 MFMA (f32 accumulate)",
+        "data": "synthetic (seeded; no dataset or weights)",
+        "config": {"workload": "%s: B=%d qlen=%d heads=%d (query buffer %d) tokens=%d kv_scale=%g splits<=%d "
+                               "workers=%d W_UV=%s" % (w.name, w.batch, w.qlen, w.heads, w.heads_pad,
+                                                         w.total_tokens, w.kv_scale, w.num_splits,
+                                                         w.num_workers, w.w_format),
+                   "global_batch": w.batch, "seq_len": int(w.lengths.max())},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
+                     "flops_per_launch": flops},
+        "roofline_hbm": {"achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs_partial / HBM_PEAK_GBS, 4), "kv_bytes_per_launch": kv_bytes},
+        "attend_us_in_step": round(float(np.mean(attn_ms)) * 1e3, 2),
+        "wall_s_timed_region": round(t_wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_budget_s)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,173 @@
+/*
+ * mla_fp8.h — C ABI of the MLA decode hot path over an fp8 latent KV cache
+ * (gfx950 / MI355X).
+ *
+ * The path, as the vLLM pages "vllm.models.kimi_k3.amd.specialized_decode.
+ * runtime.mla" (sections `pre`, `attend`, `m1c_inputs`, `post`) and
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.mla.value"
+ * (classes `MlaValue`, `MlaGate`) describe it:
+ *
+ *   mla_kv_write        new tokens' [kv_c | k_pe] rows -> fp8 cache rows
+ *   mla_decode_partial  absorbed queries attend over the paged fp8 cache:
+ *                       split-KV partials o (bf16) and LSE (f32)
+ *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
+ *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     the argument says "host".  The library keeps no pointer after a call
+ *     returns, allocates nothing, and never synchronizes: work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream).
+ *   - bf16 data is passed as uint16_t (raw bits), fp8 E4M3 (OCP "fn": bias
+ *     7, max 448, 0x7F/0xFF NaN, no infinities) as uint8_t.
+ *   - Strides are in ELEMENTS of the pointed-to type; the innermost axis of
+ *     every array is contiguous.
+ *   - Return value: MLA_OK, or an error code from the list below.  Argument
+ *     checks happen on the host before anything is enqueued; on an error
+ *     nothing is enqueued.  MLA_ERR_HIP reports a failed launch.
+ *   - Index validity (slot_mapping, kv_indices inside [0, num_slots)) is the
+ *     caller's guarantee; a cache index outside that range reads as fp8 NaN
+ *     (so it poisons the rows that use it instead of faulting).
+ */
+#ifndef MLA_FP8_H
+#define MLA_FP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_OK 0
+#define MLA_ERR_INVALID 1     /* a null pointer, bad size or bad stride   */
+#define MLA_ERR_UNSUPPORTED 2 /* valid but outside what the kernels cover */
+#define MLA_ERR_HIP 3         /* the HIP runtime reported an error        */
+
+#define MLA_D_LATENT 512 /* kv_lora_rank: value width of a cache row */
+#define MLA_D_ROPE 64    /* rope width */
+#define MLA_D_QK 576     /* one cache row: 512 latent then 64 rope   */
+#define MLA_D_V 128      /* v_head_dim: W_UV output width per head    */
+
+#define MLA_W_BF16 0
+#define MLA_W_MXFP4 1
+
+/* Text for a status code (static storage; never NULL). */
+const char* mla_status_string(int status);
+
+/*
+ * Cache write of new tokens ([MLA] `pre`: do_kv_cache_update(kv_c, k_pe,
+ * kv_cache, slots, ..., k_scale)).  Token i's cache row is
+ *   kv_cache[slot_mapping[i]][c] = E(x_c / kv_scale),  c < 576,
+ * with x = [kv_c[i][0:512] | k_pe[i][0:64]] (bf16), the division a correctly
+ * rounded binary32 division, and E the fp8 E4M3 encoder rounding to nearest
+ * even and saturating to +-448 (NaN -> 0x7F).  A negative slot skips the
+ * token.  Slots must be distinct.
+ *   kv_c         [n][kv_c_stride] bf16, first 512 used (e.g. a view of a
+ *                fused projection output, stride >= 512)
+ *   k_pe         [n][k_pe_stride] bf16, first 64 used
+ *   slot_mapping [n] int64
+ *   kv_cache     [num_slots][576] u8, rows contiguous
+ * n = 0 is a no-op.
+ */
+int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                 int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n, uint8_t* kv_cache,
+                 int64_t num_slots, float kv_scale, void* stream);
+
+/*
+ * Split-KV partial attention ([MLA] `attend`, `m1c_inputs`: partials
+ * o [splits, S, H, 512] bf16 and LSE [splits, S, H] f32, merged afterwards).
+ *
+ * Rows: S = batch * qlen query rows; row t = r*qlen + j belongs to request
+ * r.  Request r's cache rows are kv_indices[kv_indptr[r] .. kv_indptr[r+1])
+ * (page size 1, CSR), L_r = kv_indptr[r+1] - kv_indptr[r] tokens; the
+ * cache already holds the request's qlen newest tokens, and row j sees its
+ * first L_r - qlen + j + 1 tokens (causal within the speculative window).
+ *
+ * For head h < heads, over a token range [a, b) of the row's visible tokens:
+ *   s_i = sm_scale * kv_scale * sum_{d<576} q[t][h][d] * fp8(kv[row_i][d])
+ *   LSE = ln sum_i exp(s_i),   o = kv_scale * sum_i exp(s_i - LSE) * fp8(kv[row_i][0:512])
+ * The ranges are the splits: the KV token stream (kv_indices order) is cut
+ * every `chunk` tokens,
+ *   chunk = max(split_min_tokens, ceil(T / num_workers), ceil(L_max / (num_splits-1)))
+ *   (chunk = max(split_min_tokens, T) when num_splits == 1),
+ * T the total and L_max the longest request; split k of request r is its
+ * k-th piece between cuts (mla_split_plan computes the same partition on
+ * the host).  One workgroup set processes one chunk, so the work is token
+ * balanced across num_workers workers.
+ *
+ * Outputs, for every k < num_splits, t < S, h < heads:
+ *   lse_part[k*ls_split + t*ls_row + h*ls_head]          f32, -inf if split k is
+ *                                                         empty for row t
+ *   o_part[k*os_split + t*os_row + h*os_head + d]        bf16 (d < 512), written only
+ *                                                         where the LSE is finite
+ * q: [S][...][576] bf16 with strides (q_stride_row, q_stride_head); the
+ * query buffer may carry padded heads beyond `heads` (never read).
+ * kv_cache: [num_slots][576] u8.  Requires 1 <= num_splits <= 1024,
+ * num_workers >= 1, qlen >= 1, heads >= 1.
+ */
+int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
+                       int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
+                       int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
+                       float sm_scale, float kv_scale, int32_t num_splits, int32_t num_workers,
+                       int32_t split_min_tokens, uint16_t* o_part, int64_t os_split, int64_t os_row,
+                       int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row,
+                       int64_t ls_head, void* stream);
+
+/*
+ * Host helper: the split partition mla_decode_partial uses.
+ *   kv_indptr_host [batch+1] (host), split_bounds_host [batch][num_splits+1]
+ *   (host, written): split k of request r covers request-local tokens
+ *   [bounds[r][k], bounds[r][k+1]); unused splits are empty (= L_r).
+ *   *chunk_out (host, nullable) receives chunk.
+ * Pure host code: no device work, usable without a GPU.
+ */
+int mla_split_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_splits,
+                   int32_t num_workers, int32_t split_min_tokens, int32_t* split_bounds_host,
+                   int64_t* chunk_out);
+
+/*
+ * LSE merge of the split partials ([MLA] `m1c_inputs`: "M1b merges the
+ * splits"; the same combine `post` applies across ranks).  For row t, head h:
+ *   m = max_k lse_k;  m = -inf  ->  o = 0, lse = -inf;  otherwise
+ *   lse = m + ln sum_k exp(lse_k - m),   o = bf16( sum_k exp(lse_k - lse) * o_k )
+ * Splits with lse_k = -inf are skipped and their o_k is never read.
+ *   o_part   [num_splits][rows][heads][512] bf16 (strides os_split, os_row, os_head)
+ *   lse_part [num_splits][rows][heads] f32 (strides ls_split, ls_row, ls_head)
+ *   o        [rows][heads][512] bf16 (strides o_row, o_head)
+ *   lse      [rows][heads] f32 (strides l_row, l_head), nullable
+ * rows = 0 is a no-op.
+ */
+int mla_merge_lse(const uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                  const float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                  int32_t num_splits, int32_t rows, int32_t heads, uint16_t* o, int64_t o_row,
+                  int64_t o_head, float* lse, int64_t l_row, int64_t l_head, void* stream);
+
+/*
+ * W_UV value projection + sigmoid gate ([VALUE] `MlaValue` and `MlaGate`;
+ * [MLA] `post`).  For row t (request t / qlen), head h, v < 128:
+ *   acc = sum_{l<512} latent[t][h][l] * W(h, v, l)          (f32 accumulation)
+ *   out[t][h*128 + v] = bf16( f32(bf16(acc)) * sigmoid_f32(gate[t][h*128 + v]) )
+ * when lengths[t / qlen] > 0, and +0 otherwise (even for a NaN gate).
+ *   latent [rows][heads][512] bf16 (strides l_row, l_head)
+ *   w_format MLA_W_BF16: w_uv = bf16 [heads][128][512] (strides w_head, w_v;
+ *            the latent axis contiguous, as the absorbed kv_b_proj view)
+ *   w_format MLA_W_MXFP4: w_uv = u8 E2M1 codes [heads][128][256] (strides in
+ *            bytes w_head, w_v; element 2k in the low nibble of byte k),
+ *            w_scale = u8 E8M0 [heads][128][16] (strides ws_head, ws_v), one
+ *            scale per 32 consecutive latents: W = e2m1 * 2^(e8m0 - 127)
+ *   gate   [rows][heads*128] bf16 logits (stride g_row)
+ *   lengths [rows / qlen] int32
+ *   out    [rows][heads*128] bf16 (stride out_row)
+ * rows must be a multiple of qlen; rows = 0 is a no-op.
+ */
+int mla_value_gate(const uint16_t* latent, int64_t l_row, int64_t l_head, int32_t w_format,
+                   const void* w_uv, int64_t w_head, int64_t w_v, const uint8_t* w_scale,
+                   int64_t ws_head, int64_t ws_v, const uint16_t* gate, int64_t g_row,
+                   const int32_t* lengths, int32_t rows, int32_t qlen, int32_t heads,
+                   uint16_t* out, int64_t out_row, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_FP8_H */

@@ -1,0 +1,173 @@
+"""MLA decode over an fp8 latent KV cache on MI355X (gfx950).
+
+A thin Python binding of the C ABI in include/mla_fp8.h (libmla_fp8.so,
+built by ``mla_latent_kv_fp8_amd.build``).  Functions here only check
+arguments and marshal torch tensors into pointers, strides and the current
+HIP stream; every step of the path runs in the library's HIP kernels.  There
+is no fallback: if the library is missing, the first call raises.
+
+The path (vLLM pages "vllm.models.kimi_k3.amd.specialized_decode.runtime.mla"
+and "...nvidia.specialized_decode.cutedsl.mla.value"):
+  kv_write -> decode_partial -> merge_lse -> value_gate.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+D_LATENT, D_ROPE, D_QK, D_V = 512, 64, 576, 128
+W_BF16, W_MXFP4 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_fp8.so")
+_lib = None
+
+
+class MlaError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmla_fp8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MlaError("libmla_fp8.so is not built (python -m mla_latent_kv_fp8_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.mla_status_string.argtypes = [ctypes.c_int]
+        L.mla_status_string.restype = ctypes.c_char_p
+        L.mla_kv_write.argtypes = [P, i64, P, i64, P, i32, P, i64, f32, P]
+        L.mla_decode_partial.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32,
+                                         i32, P, i64, i64, i64, P, i64, i64, i64, P]
+        L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.mla_merge_lse.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, i32, P, i64, i64, P,
+                                    i64, i64, P]
+        L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
+                                     P, i64, P]
+        for name in ("mla_kv_write", "mla_decode_partial", "mla_split_plan", "mla_merge_lse",
+                     "mla_value_gate"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MlaError("%s: %s" % (what, lib().mla_status_string(status).decode()))
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise MlaError("%s must be a CUDA (HIP) tensor" % name)
+    if t.dtype not in dtypes:
+        raise MlaError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise MlaError("%s: the innermost axis must be contiguous" % name)
+    return t.data_ptr()
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def kv_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor, kv_cache: torch.Tensor,
+             kv_scale: float) -> None:
+    """Write n new tokens' rows E([kv_c | k_pe] / kv_scale) into kv_cache
+    [num_slots, 576] at slot_mapping (int64; negative = skip)."""
+    n = slot_mapping.shape[0]
+    assert kv_c.shape[0] == n and k_pe.shape[0] == n
+    assert kv_c.shape[-1] >= D_LATENT and k_pe.shape[-1] >= D_ROPE and kv_cache.shape[-1] == D_QK
+    st = lib().mla_kv_write(_dev(kv_c, "kv_c", _BF16), kv_c.stride(0), _dev(k_pe, "k_pe", _BF16),
+                            k_pe.stride(0), _dev(slot_mapping, "slot_mapping", (torch.int64,)), n,
+                            _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0], float(kv_scale),
+                            _stream())
+    _check(st, "mla_kv_write")
+
+
+def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,
+                   kv_indices: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor, *, qlen: int,
+                   heads: int, sm_scale: float, kv_scale: float, num_workers: int = 256,
+                   split_min_tokens: int = 256) -> None:
+    """Split-KV partials: q [S, H_pad, 576] bf16 (first `heads` used) over
+    kv_cache [num_slots, 576] u8 with CSR (kv_indptr [B+1], kv_indices) int32
+    -> o_part [splits, S, heads, 512] bf16, lse_part [splits, S, heads] f32
+    (strided views allowed)."""
+    S = q.shape[0]
+    batch = kv_indptr.shape[0] - 1
+    if S != batch * qlen:
+        raise MlaError("q has %d rows, expected batch*qlen = %d" % (S, batch * qlen))
+    ns = o_part.shape[0]
+    if lse_part.shape[0] != ns or o_part.shape[1] < S or o_part.shape[2] < heads or o_part.shape[3] != D_LATENT:
+        raise MlaError("bad partial buffer shapes")
+    if q.shape[-1] != D_QK or q.shape[1] < heads:
+        raise MlaError("q must be [S, >=heads, 576]")
+    st = lib().mla_decode_partial(
+        _dev(q, "q", _BF16), q.stride(0), q.stride(1), batch, qlen, heads,
+        _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0],
+        _dev(kv_indptr, "kv_indptr", (torch.int32,)), _dev(kv_indices, "kv_indices", (torch.int32,)),
+        float(sm_scale), float(kv_scale), ns, int(num_workers), int(split_min_tokens),
+        _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
+        _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
+        lse_part.stride(2), _stream())
+    _check(st, "mla_decode_partial")
+
+
+def split_plan(kv_indptr, num_splits: int, num_workers: int, split_min_tokens: int):
+    """Host-side split partition (no GPU): returns (bounds [B, splits+1] int32, chunk)."""
+    indptr = np.ascontiguousarray(np.asarray(kv_indptr), dtype=np.int32)
+    batch = indptr.shape[0] - 1
+    bounds = np.zeros((batch, num_splits + 1), dtype=np.int32)
+    chunk = ctypes.c_int64(0)
+    st = lib().mla_split_plan(indptr.ctypes.data_as(ctypes.c_void_p), batch, num_splits, num_workers,
+                              split_min_tokens, bounds.ctypes.data_as(ctypes.c_void_p), ctypes.byref(chunk))
+    _check(st, "mla_split_plan")
+    return bounds, int(chunk.value)
+
+
+def merge_lse(o_part: torch.Tensor, lse_part: torch.Tensor, o: torch.Tensor, lse: torch.Tensor | None = None) -> None:
+    """LSE merge: o_part [splits, rows, heads, 512], lse_part [splits, rows, heads]
+    -> o [rows, heads, 512] bf16 (+ lse [rows, heads] f32)."""
+    ns, rows, heads = lse_part.shape
+    if o.shape[0] < rows or o.shape[1] < heads:
+        raise MlaError("bad output shape")
+    lp = 0 if lse is None else _dev(lse, "lse", (torch.float32,))
+    st = lib().mla_merge_lse(
+        _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
+        _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
+        lse_part.stride(2), ns, rows, heads, _dev(o, "o", _BF16), o.stride(0), o.stride(1),
+        ctypes.c_void_p(lp), 0 if lse is None else lse.stride(0), 0 if lse is None else lse.stride(1),
+        _stream())
+    _check(st, "mla_merge_lse")
+
+
+def value_gate(latent: torch.Tensor, gate: torch.Tensor, lengths: torch.Tensor, out: torch.Tensor, *,
+               qlen: int, w_uv: torch.Tensor | None = None, w_fp4: torch.Tensor | None = None,
+               w_scale: torch.Tensor | None = None) -> None:
+    """W_UV + sigmoid gate: latent [rows, heads, 512] bf16 -> out [rows, heads*128] bf16.
+    Weights: w_uv bf16 [heads, 128, 512], or w_fp4 u8 [heads, 128, 256] with
+    w_scale u8 [heads, 128, 16]."""
+    rows, heads = latent.shape[0], latent.shape[1]
+    if w_uv is not None:
+        fmt, wp, wh, wv = W_BF16, _dev(w_uv, "w_uv", _BF16), w_uv.stride(0), w_uv.stride(1)
+        sp, sh, sv = 0, 0, 0
+        if w_uv.shape[0] < heads or w_uv.shape[1] != D_V or w_uv.shape[2] != D_LATENT:
+            raise MlaError("w_uv must be [heads, 128, 512]")
+    else:
+        fmt, wp, wh, wv = W_MXFP4, _dev(w_fp4, "w_fp4", (torch.uint8,)), w_fp4.stride(0), w_fp4.stride(1)
+        sp, sh, sv = _dev(w_scale, "w_scale", (torch.uint8,)), w_scale.stride(0), w_scale.stride(1)
+        if w_fp4.shape[0] < heads or w_fp4.shape[1] != D_V or w_fp4.shape[2] != D_LATENT // 2:
+            raise MlaError("w_fp4 must be [heads, 128, 256]")
+    st = lib().mla_value_gate(
+        _dev(latent, "latent", _BF16), latent.stride(0), latent.stride(1), fmt, ctypes.c_void_p(wp), wh, wv,
+        ctypes.c_void_p(sp), sh, sv, _dev(gate, "gate", _BF16), gate.stride(0),
+        _dev(lengths, "lengths", (torch.int32,)), rows, qlen, heads, _dev(out, "out", _BF16), out.stride(0),
+        _stream())
+    _check(st, "mla_value_gate")

@@ -1,0 +1,106 @@
+// Shared device helpers for the gfx950 MLA decode kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mla_fp8.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ conversions
+
+// 4 fp8 E4M3 bytes (one dword, byte 0 first) -> 4 bf16, exactly (E4M3 fits
+// in bf16).  v_cvt_scalef32_pk_bf16_fp8 converts bytes {0,1} (word 0) or
+// {2,3} (word 1) with a binary32 scale of 1.
+__device__ __forceinline__ bf16x4 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(u32x2 w) {
+  bf16x4 a = fp8x4_to_bf16x4(w[0]);
+  bf16x4 b = fp8x4_to_bf16x4(w[1]);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// 8 E2M1 codes (one dword: byte k holds elements 2k (low nibble) and 2k+1)
+// times a binary32 scale -> 8 bf16.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// E8M0 scale byte -> binary32 2^(b-127) (b = 0 is the subnormal 2^-127,
+// b = 255 NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  uint32_t bits = b == 0 ? 0x00400000u : (b == 255 ? 0x7FC00000u : (b << 23));
+  return __uint_as_float(bits);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// binary32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// C[16x16] += A[16x32] * B[32x16], bf16 in, f32 accumulate.  Lane l holds
+// A row l%16, k 8*(l/16)..+7; B column l%16, same k; C rows 4*(l/16)..+3 of
+// column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+// ------------------------------------------------------------ split plan
+
+// The split partition of mla_decode_partial, shared by the device kernel
+// and the host helper: `chunk` from the token total T, the longest request
+// and the caller's bounds.
+__host__ __device__ __forceinline__ int64_t split_chunk(int64_t T, int64_t lmax, int32_t num_splits,
+                                                        int32_t num_workers, int32_t split_min) {
+  int64_t chunk = split_min > 1 ? split_min : 1;
+  if (num_splits > 1) {
+    int64_t a = (T + num_workers - 1) / num_workers;
+    int64_t b = (lmax + num_splits - 2) / (num_splits - 1);
+    if (a > chunk) chunk = a;
+    if (b > chunk) chunk = b;
+  } else if (T > chunk) {
+    chunk = T;
+  }
+  return chunk;
+}
+
+}  // namespace mla

@@ -1,0 +1,89 @@
+// Cache write of new tokens: bf16 [kv_c | k_pe] rows -> fp8 E4M3 cache rows
+// (the do_kv_cache_update step of the decode runtime's `pre`).
+#include "common.hpp"
+
+namespace mla {
+
+// binary32 -> fp8 E4M3 (OCP fn): round to nearest even, saturate to +-448,
+// NaN -> 0x7F.
+__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;
+  float av = __uint_as_float(a);
+  uint32_t code;
+  if (av < 0.015625f) {
+    // subnormal range: quantum 2^-9; rint rounds ties to even; 8 -> 0x08 (2^-6)
+    code = (uint32_t)__builtin_rintf(av * 512.0f);
+  } else {
+    // keep 3 mantissa bits, nearest even (carry may bump the exponent)
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    int e = (int)(r >> 23) - 127 + 7;
+    uint32_t m = (r >> 20) & 7u;
+    if (e > 15 || (e == 15 && m == 7)) {
+      code = 0x7Eu;  // saturate (448)
+    } else {
+      code = ((uint32_t)e << 3) | m;
+    }
+  }
+  return code | sign;
+}
+
+// One thread per 8 consecutive columns of one token: 72 threads per row.
+__global__ void __launch_bounds__(256) kv_write_kernel(const uint16_t* __restrict__ kv_c,
+                                                       int64_t kv_c_stride,
+                                                       const uint16_t* __restrict__ k_pe,
+                                                       int64_t k_pe_stride,
+                                                       const int64_t* __restrict__ slots, int32_t n,
+                                                       uint8_t* __restrict__ cache, int64_t num_slots,
+                                                       float kv_scale) {
+  int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= (int64_t)n * 72) return;
+  int64_t i = item / 72;
+  int c0 = (int)(item % 72) * 8;
+  int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
+  const uint16_t* src = c0 < MLA_D_LATENT ? kv_c + i * kv_c_stride + c0
+                                          : k_pe + i * k_pe_stride + (c0 - MLA_D_LATENT);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = bf16_bits_to_f32(src[e]);
+    uint32_t b = f32_to_fp8_e4m3(x / kv_scale);  // correctly rounded binary32 division
+    if (e < 4)
+      lo |= b << (8 * e);
+    else
+      hi |= b << (8 * (e - 4));
+  }
+  *reinterpret_cast<u32x2*>(cache + slot * MLA_D_QK + c0) = u32x2{lo, hi};
+}
+
+}  // namespace mla
+
+extern "C" const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                            int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n,
+                            uint8_t* kv_cache, int64_t num_slots, float kv_scale, void* stream) {
+  if (n < 0 || num_slots < 0) return MLA_ERR_INVALID;
+  if (n == 0) return MLA_OK;
+  if (!kv_c || !k_pe || !slot_mapping || !kv_cache) return MLA_ERR_INVALID;
+  if (kv_c_stride < MLA_D_LATENT || k_pe_stride < MLA_D_ROPE) return MLA_ERR_INVALID;
+  if (!(kv_scale > 0.0f) || !__builtin_isfinite(kv_scale)) return MLA_ERR_INVALID;
+  int64_t items = (int64_t)n * 72;
+  int64_t blocks = (items + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(mla::kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, n, kv_cache, num_slots,
+                     kv_scale);
+  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}

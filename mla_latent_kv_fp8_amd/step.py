@@ -1,0 +1,80 @@
+"""One decode step of the path on device buffers: kv_write -> decode_partial
+-> merge_lse -> value_gate, for a synthetic workload (see synth.py).
+
+Buffers are allocated once by `DeviceStep.__init__` (torch, on the current
+device) and reused by every `run()`, so a timed step enqueues the four
+library calls and nothing else.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import D_LATENT, D_QK, D_V, decode_partial, kv_write, merge_lse, value_gate
+from .synth import FP8_NAN, Workload
+
+
+def _bf16_dev(a: np.ndarray, dev) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+class DeviceStep:
+    def __init__(self, w: Workload, device="cuda", num_workers: int | None = None,
+                 split_min_tokens: int | None = None, fill_cache: bool = True):
+        self.w = w
+        dev = torch.device(device)
+        self.dev = dev
+        self.num_workers = num_workers or w.num_workers
+        self.split_min = split_min_tokens if split_min_tokens is not None else w.split_min_tokens
+        S, H, VH = w.S, w.heads, w.value_heads
+        self.q = _bf16_dev(w.q, dev)
+        self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
+        self.indptr = torch.from_numpy(w.indptr).to(dev)
+        self.indices = torch.from_numpy(w.indices).to(dev)
+        self.lengths = torch.from_numpy(w.lengths).to(dev)
+        if fill_cache and w.kv_rows is not None and w.total_tokens > 0:
+            rows = _bf16_dev(w.kv_rows, dev)
+            slots = torch.from_numpy(w.indices.astype(np.int64)).to(dev)
+            kv_write(rows[:, :D_LATENT], rows[:, D_LATENT:], slots, self.kv_cache, w.kv_scale)
+            del rows
+        self.new_rows = _bf16_dev(w.new_rows, dev)
+        self.slot_mapping = torch.from_numpy(w.slot_mapping).to(dev)
+        self.o_part = torch.empty((w.num_splits, S, H, D_LATENT), dtype=torch.bfloat16, device=dev)
+        self.lse_part = torch.empty((w.num_splits, S, H), dtype=torch.float32, device=dev)
+        # the W_UV stage may run on more heads than the attention (the extra
+        # heads' latent rows are synthetic)
+        self.latent = torch.zeros((S, VH, D_LATENT), dtype=torch.bfloat16, device=dev)
+        if VH > H:
+            self.latent[:, H:, :] = _bf16_dev(w.extra_latent, dev)
+        self.lse = torch.empty((S, H), dtype=torch.float32, device=dev)
+        self.gate = _bf16_dev(w.gate, dev)
+        self.out = torch.empty((S, VH * D_V), dtype=torch.bfloat16, device=dev)
+        self.w_uv = _bf16_dev(w.w_uv, dev) if w.w_uv is not None else None
+        self.w_fp4 = torch.from_numpy(w.w_fp4).to(dev) if w.w_fp4 is not None else None
+        self.w_scale = torch.from_numpy(w.w_scale).to(dev) if w.w_scale is not None else None
+
+    # the four calls ---------------------------------------------------------
+    def write_new_tokens(self):
+        nr = self.new_rows
+        kv_write(nr[:, :D_LATENT], nr[:, D_LATENT:], self.slot_mapping, self.kv_cache, self.w.kv_scale)
+
+    def attend(self):
+        w = self.w
+        decode_partial(self.q, self.kv_cache, self.indptr, self.indices, self.o_part, self.lse_part,
+                       qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
+                       num_workers=self.num_workers, split_min_tokens=self.split_min)
+
+    def merge(self):
+        merge_lse(self.o_part, self.lse_part, self.latent[:, :self.w.heads], self.lse)
+
+    def value(self):
+        w = self.w
+        value_gate(self.latent, self.gate, self.lengths, self.out, qlen=w.qlen, w_uv=self.w_uv,
+                   w_fp4=self.w_fp4, w_scale=self.w_scale)
+
+    def run(self, write_new: bool = True):
+        if write_new:
+            self.write_new_tokens()
+        self.attend()
+        self.merge()
+        self.value()

@@ -1,0 +1,98 @@
+"""CPU checks of the C ABI: the library loads and exports every entry point
+the header declares, the host split plan matches the oracle's partition,
+and argument errors are reported before any device work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_fp8.h")
+
+
+@pytest.fixture(scope="module")
+def mlib():
+    import mla_latent_kv_fp8_amd as m
+
+    if not os.path.exists(m.LIB_PATH):
+        from mla_latent_kv_fp8_amd import build
+
+        build.build()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(mla_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for n in ["mla_kv_write", "mla_decode_partial", "mla_merge_lse", "mla_value_gate", "mla_split_plan",
+              "mla_status_string"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(mlib):
+    L = mlib.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings(mlib):
+    L = mlib.lib()
+    assert L.mla_status_string(0) == b"ok"
+    assert L.mla_status_string(1) == b"invalid argument"
+    assert L.mla_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("lens,ns,W,mn", [
+    ([37, 64], 2, 256, 1),
+    ([1024, 8192, 0, 4000, 17], 16, 256, 256),
+    ([5, 0, 0, 9], 3, 4, 1),
+    ([100000, 3, 64000], 64, 256, 256),
+    ([10, 20, 30], 1, 256, 1),
+    ([0, 0], 4, 8, 1),
+])
+def test_split_plan_matches_oracle(mlib, oracle, lens, ns, W, mn):
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    b, chunk = mlib.split_plan(indptr, ns, W, mn)
+    ob, ochunk = oracle.split_bounds(indptr, ns, W, mn)
+    assert chunk == ochunk and np.array_equal(b, ob)
+
+
+def test_split_plan_random_matches_oracle(mlib, oracle):
+    rng = np.random.default_rng(0)
+    for _ in range(200):
+        B = int(rng.integers(1, 40))
+        lens = rng.integers(0, 5000, B)
+        lens[rng.random(B) < 0.2] = 0
+        indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        ns, W, mn = int(rng.integers(1, 70)), int(rng.integers(1, 300)), int(rng.integers(1, 600))
+        b, chunk = mlib.split_plan(indptr, ns, W, mn)
+        ob, ochunk = oracle.split_bounds(indptr, ns, W, mn)
+        assert chunk == ochunk and np.array_equal(b, ob)
+
+
+def test_argument_errors_before_device_work(mlib):
+    L = mlib.lib()
+    null = ctypes.c_void_p(0)
+    # null pointers / bad sizes are rejected on the host (no launch happens)
+    assert L.mla_kv_write(null, 512, null, 64, null, 4, null, 10, 1.0, null) == 1
+    assert L.mla_kv_write(null, 512, null, 64, null, 0, null, 10, 1.0, null) == 0  # n = 0: no-op
+    assert L.mla_decode_partial(null, 576, 576, 2, 1, 16, null, 10, null, null, 0.1, 1.0, 2, 8, 1,
+                                null, 0, 0, 0, null, 0, 0, 0, null) == 1
+    assert L.mla_decode_partial(null, 576, 576, 2, 0, 16, null, 10, null, null, 0.1, 1.0, 2, 8, 1,
+                                null, 0, 0, 0, null, 0, 0, 0, null) == 1  # qlen 0
+    assert L.mla_merge_lse(null, 0, 0, 0, null, 0, 0, 0, 0, 4, 4, null, 0, 0, null, 0, 0, null) == 1
+    assert L.mla_merge_lse(null, 0, 0, 0, null, 0, 0, 0, 2, 0, 4, null, 0, 0, null, 0, 0, null) == 0
+    assert L.mla_value_gate(null, 0, 0, 0, null, 0, 0, null, 0, 0, null, 0, null, 6, 4, 2, null, 0,
+                            null) == 1  # rows not a multiple of qlen
+    assert L.mla_value_gate(null, 0, 0, 7, null, 0, 0, null, 0, 0, null, 0, null, 8, 4, 2, null, 0,
+                            null) == 1
+    indptr = np.array([0, 5, 3], dtype=np.int32)  # negative length
+    bounds = np.zeros((2, 3), np.int32)
+    assert L.mla_split_plan(indptr.ctypes.data_as(ctypes.c_void_p), 2, 2, 4, 1,
+                            bounds.ctypes.data_as(ctypes.c_void_p), null) == 1

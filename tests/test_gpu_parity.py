@@ -1,0 +1,421 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: kv_write bytes and split indexing bit-exact; partial o within 1e-2
+(abs, after bf16 rounding) and LSE within 1e-3 (-inf must match); merged
+latent the same; gated output max|err| <= 2e-2 * max|ref|.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+O_TOL, LSE_TOL, OUT_REL_TOL = 1e-2, 1e-3, 2e-2
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_latent_kv_fp8_amd as m
+
+    m.lib()  # raises if the HIP library is missing: no fallback
+    return m
+
+
+def _np_bf16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _bf16_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _announce(msg):
+    print("[case]", msg, flush=True)
+
+
+# ------------------------------------------------------------------ kv_write
+
+def test_kv_write_bitexact_edge_values(ops, oracle):
+    _announce("kv_write edge values")
+    rng = np.random.default_rng(100)
+    n, slots = 300, 401
+    x = (rng.standard_normal((n, 576)) * 40).astype(np.float32)
+    # ties of E4M3 at several binades, saturation, NaN, tiny values, -0
+    pos = np.arange(0, 0x7F, dtype=np.uint8)
+    pv = oracle.fp8_decode(pos)
+    mids = ((pv[:-1] + pv[1:]) / 2).astype(np.float32)
+    x[0, :len(mids)] = mids
+    x[1, :len(mids)] = -mids
+    x[2, :8] = [448, 449, 464, 465, 1e30, -1e30, np.inf, -np.inf]
+    x[2, 8:12] = [np.nan, -0.0, 1e-30, -1e-6]
+    from mla_latent_kv_fp8_amd.synth import to_bf16_bits
+    bits = to_bf16_bits(x)
+    fused = np.zeros((n, 2112), dtype=np.uint16)  # strided views of a fused projection
+    fused[:, 1536:2048] = bits[:, :512]
+    fused[:, 2048:2112] = bits[:, 512:]
+    slot_map = rng.permutation(slots)[:n].astype(np.int64)
+    slot_map[5] = -1
+    for kv_scale in (1.0, 0.05, 3.0):
+        cache = torch.full((slots, 576), 0x7F, dtype=torch.uint8, device="cuda")
+        f = _bf16_dev(fused)
+        ops.kv_write(f[:, 1536:2048], f[:, 2048:], torch.from_numpy(slot_map).cuda(), cache, kv_scale)
+        torch.cuda.synchronize()
+        want = oracle.kv_write(fused[:, 1536:2048], fused[:, 2048:], slot_map,
+                               np.full((slots, 576), 0x7F, np.uint8), kv_scale)
+        assert np.array_equal(cache.cpu().numpy(), want), kv_scale
+
+
+# ----------------------------------------------------------- helpers
+
+def _oracle_cache(oracle, w, requests=None):
+    """Cache bytes the oracle writes (all rows, or only the rows of the
+    given requests), then the step's new tokens."""
+    cache = np.full((w.num_slots, 576), 0x7F, np.uint8)
+    if requests is None:
+        sel = np.arange(w.total_tokens)
+    else:
+        sel = np.concatenate([np.arange(w.indptr[r], w.indptr[r + 1]) for r in requests] + [np.zeros(0, int)])
+    rows = w.kv_rows[sel]
+    cache = oracle.kv_write(rows[:, :512], rows[:, 512:], w.indices[sel].astype(np.int64), cache, w.kv_scale)
+    sm = w.slot_mapping.copy()
+    if requests is not None:
+        keep = np.zeros(len(sm), bool)
+        per = len(sm) // w.batch
+        for r in requests:
+            keep[r * per:(r + 1) * per] = True
+        sm[~keep] = -1
+    cache = oracle.kv_write(w.new_rows[:, :512], w.new_rows[:, 512:], sm, cache, w.kv_scale)
+    return cache
+
+
+def _run_step(ops, w, **kw):
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    st = DeviceStep(w, **kw)
+    st.run()
+    torch.cuda.synchronize()
+    return st
+
+
+def _check_partials(oracle, w, st, cache):
+    H = w.heads
+    bounds, chunk = oracle.split_bounds(w.indptr, w.num_splits, st.num_workers, st.split_min)
+    import mla_latent_kv_fp8_amd as m
+
+    lib_bounds, lib_chunk = m.split_plan(w.indptr, w.num_splits, st.num_workers, st.split_min)
+    assert lib_chunk == chunk and np.array_equal(lib_bounds, bounds)
+    q = np.ascontiguousarray(w.q[:, :H])
+    o_ref, l_ref = oracle.decode_partial(q, cache, w.indptr, w.indices, bounds, w.qlen, w.sm_scale, w.kv_scale)
+    lse = st.lse_part.cpu().numpy().astype(np.float64)
+    o = oracle.bf16_decode(_np_bf16(st.o_part))
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(lse), ~fin), "empty-split pattern differs"
+    assert np.abs(lse[fin] - l_ref[fin]).max(initial=0) <= LSE_TOL
+    o_ref_b = oracle.bf16_decode(oracle.bf16_round(o_ref))
+    err = np.abs(o[fin] - o_ref_b[fin]).max(initial=0)
+    assert err <= O_TOL, err
+    return bounds
+
+
+def _check_merge_and_value(oracle, w, st):
+    H, VH = w.heads, w.value_heads
+    o_part = _np_bf16(st.o_part)
+    lse_part = st.lse_part.cpu().numpy()
+    # merge, on the GPU's own partials (same inputs on both sides)
+    mo, ml = oracle.merge_lse(np.where(np.isfinite(lse_part)[..., None], o_part, 0), lse_part)
+    lat = _np_bf16(st.latent)
+    got = oracle.bf16_decode(lat[:, :H])
+    want = oracle.bf16_decode(oracle.bf16_round(mo))
+    assert np.abs(got - want).max(initial=0) <= O_TOL
+    gl = st.lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(gl), np.isneginf(ml))
+    fin = np.isfinite(ml)
+    assert np.abs(gl[fin] - ml[fin]).max(initial=0) <= LSE_TOL
+    # value + gate, on the GPU's latent
+    _, out_ref = oracle.value_gate(lat, w.gate, w.lengths, w.qlen, w_bf16=w.w_uv, w_fp4=w.w_fp4,
+                                   w_scale=w.w_scale)
+    out = _np_bf16(st.out)
+    ref = oracle.bf16_decode(out_ref)
+    dev = oracle.bf16_decode(out)
+    scale = np.abs(ref).max()
+    assert np.abs(dev - ref).max() <= OUT_REL_TOL * scale
+    empty_rows = np.repeat(w.lengths == 0, w.qlen)
+    assert (out[empty_rows] == 0).all(), "rows of empty requests must be +0"
+    assert not np.isnan(dev[~empty_rows]).any()
+
+
+# ------------------------------------------------------- small full parity
+
+SMALL = [
+    # name, batch override, length range, num_workers, split_min
+    ("tiny", None, None, None, None),
+    ("batch", 6, (100, 700), 8, 16),
+    ("batch", 5, (1, 70), 16, 1),
+    ("spec_q4", 3, (60, 300), 4, 16),
+    ("spec_q8", 2, (64, 200), 4, 8),
+    ("long", 2, (900, 1500), 16, 64),
+    ("rank_share", 4, (100, 500), 8, 32),
+]
+
+
+@pytest.mark.parametrize("name,batch,lr,nw,smin", SMALL)
+def test_step_parity_small(ops, oracle, name, batch, lr, nw, smin):
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce(f"step parity {name} batch={batch} lengths={lr} workers={nw} min={smin}")
+    w = synth.make(name, batch=batch, len_range=lr)
+    st = _run_step(ops, w, num_workers=nw, split_min_tokens=smin)
+    cache = _oracle_cache(oracle, w)
+    assert np.array_equal(st.kv_cache.cpu().numpy(), cache), "cache bytes differ"
+    _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
+
+
+def test_end_to_end_chain_tiny(ops, oracle):
+    """The oracle's own chain (its partials -> its merge -> its value) against
+    the GPU chain, from the same inputs."""
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce("end-to-end chain tiny")
+    w = synth.make("tiny")
+    st = _run_step(ops, w)
+    cache = _oracle_cache(oracle, w)
+    bounds, _ = oracle.split_bounds(w.indptr, w.num_splits, st.num_workers, st.split_min)
+    o, l = oracle.decode_partial(w.q, cache, w.indptr, w.indices, bounds, w.qlen, w.sm_scale, w.kv_scale)
+    ob = oracle.bf16_round(o)
+    mo, ml = oracle.merge_lse(ob, l.astype(np.float32))
+    lat = oracle.bf16_round(mo)
+    _, out_ref = oracle.value_gate(lat, w.gate, w.lengths, w.qlen, w_bf16=w.w_uv)
+    ref = oracle.bf16_decode(out_ref)
+    got = oracle.bf16_decode(_np_bf16(st.out))
+    assert np.abs(got - ref).max() <= OUT_REL_TOL * np.abs(ref).max()
+
+
+# ------------------------------------------------------------- merge alone
+
+@pytest.mark.parametrize("ns,rows,heads", [(1, 7, 3), (2, 5, 16), (16, 9, 12), (64, 3, 5), (70, 2, 4)])
+def test_merge_parity(ops, oracle, ns, rows, heads):
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce(f"merge ns={ns} rows={rows} heads={heads}")
+    rng = np.random.default_rng(ns * 31 + rows)
+    o, l = synth.random_partials(rng, ns, rows, heads, p_empty=0.3)
+    l[:, 0, 0] = -np.inf  # a fully empty (row, head)
+    # strided device views: pad heads and the split stride
+    o_dev = torch.zeros((ns, rows, heads + 3, 512), dtype=torch.bfloat16, device="cuda")
+    o_dev[:, :, :heads] = _bf16_dev(o)
+    l_dev = torch.zeros((ns, rows, heads + 1), dtype=torch.float32, device="cuda")
+    l_dev[:, :, :heads] = torch.from_numpy(l).cuda()
+    out = torch.full((rows, heads, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    ops.merge_lse(o_dev[:, :, :heads], l_dev[:, :, :heads], out, lse)
+    torch.cuda.synchronize()
+    mo, ml = oracle.merge_lse(np.where(np.isfinite(l)[..., None], o, 0), l)
+    got = _np_bf16(out)
+    if ns == 1:  # a single split passes through bit-exactly
+        fin = np.isfinite(l[0])
+        assert np.array_equal(got[fin], o[0][fin])
+        assert np.array_equal(lse.cpu().numpy()[fin], l[0][fin])
+    err = np.abs(oracle.bf16_decode(got) - oracle.bf16_decode(oracle.bf16_round(mo))).max()
+    assert err <= O_TOL
+    g = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(g), np.isneginf(ml))
+    fin = np.isfinite(ml)
+    assert np.abs(g[fin] - ml[fin]).max() <= LSE_TOL
+    assert (got[~fin] == 0).all()
+
+
+# -------------------------------------------------------------- value alone
+
+@pytest.mark.parametrize("fmt,rows,qlen,heads", [("bf16", 64, 1, 96), ("bf16", 13, 1, 5), ("mxfp4", 256, 4, 96),
+                                                 ("mxfp4", 20, 4, 3)])
+def test_value_gate_parity(ops, oracle, fmt, rows, qlen, heads):
+    from mla_latent_kv_fp8_amd.synth import to_bf16_bits, BF16_NAN
+
+    _announce(f"value_gate {fmt} rows={rows} qlen={qlen} heads={heads}")
+    rng = np.random.default_rng(rows + heads)
+    B = rows // qlen
+    lengths = rng.integers(0, 5, B).astype(np.int32)
+    lengths[0] = 0
+    lat = to_bf16_bits(rng.standard_normal((rows, heads, 512)).astype(np.float32) * 0.3)
+    gate = to_bf16_bits(rng.standard_normal((rows, heads * 128)).astype(np.float32))
+    gate[:, :7] = 0  # logit 0: the output is exactly bf16(acc) / 2
+    empty = np.repeat(lengths == 0, qlen)
+    gate[empty] = BF16_NAN
+    lat[empty] = BF16_NAN
+    out = torch.full((rows, heads * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    if fmt == "bf16":
+        wuv = to_bf16_bits(rng.standard_normal((heads, 128, 512)).astype(np.float32) * 0.044)
+        ops.value_gate(_bf16_dev(lat), _bf16_dev(gate), torch.from_numpy(lengths).cuda(), out, qlen=qlen,
+                       w_uv=_bf16_dev(wuv))
+        acc, ref = oracle.value_gate(lat, gate, lengths, qlen, w_bf16=wuv)
+    else:
+        w4 = rng.integers(0, 256, (heads, 128, 256), dtype=np.uint8)
+        ws = rng.integers(118, 125, (heads, 128, 16)).astype(np.uint8)
+        ops.value_gate(_bf16_dev(lat), _bf16_dev(gate), torch.from_numpy(lengths).cuda(), out, qlen=qlen,
+                       w_fp4=torch.from_numpy(w4).cuda(), w_scale=torch.from_numpy(ws).cuda())
+        acc, ref = oracle.value_gate(lat, gate, lengths, qlen, w_fp4=w4, w_scale=ws)
+    torch.cuda.synchronize()
+    got = _np_bf16(out)
+    assert (got[empty] == 0).all()
+    g, r = oracle.bf16_decode(got[~empty]), oracle.bf16_decode(ref[~empty])
+    assert np.abs(g - r).max() <= OUT_REL_TOL * np.abs(r).max()
+    # gate logit 0 -> exactly half of the bf16 value (GPU value = own bf16(acc))
+    half = got[~empty][:, :7]
+    assert np.all(np.isfinite(oracle.bf16_decode(half)))
+
+
+# ------------------------------------------------------- invariants / edges
+
+def test_page_table_permutation_bitwise(ops):
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("page-table permutation")
+    w = synth.make("batch", batch=4, len_range=(200, 600))
+    a = DeviceStep(w, num_workers=8, split_min_tokens=32)
+    a.attend(); a.merge()
+    rng = np.random.default_rng(5)
+    perm = torch.from_numpy(rng.permutation(w.num_slots)).cuda()
+    b = DeviceStep(w, num_workers=8, split_min_tokens=32)
+    kv2 = torch.empty_like(b.kv_cache)
+    kv2[perm] = b.kv_cache
+    b.kv_cache = kv2
+    b.indices = perm[b.indices.long()].to(torch.int32)
+    b.attend(); b.merge()
+    torch.cuda.synchronize()
+    assert torch.equal(a.latent.view(torch.int16), b.latent.view(torch.int16))
+    assert torch.equal(a.lse_part, b.lse_part)
+
+
+def test_determinism_and_canaries(ops):
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("determinism + NaN canaries (batch config, reduced lengths)")
+    w = synth.make("batch", batch=16, len_range=(1, 3000))
+    st = DeviceStep(w, num_workers=64, split_min_tokens=64)
+    st.run()
+    o1 = st.out.clone(); l1 = st.lse_part.clone()
+    st.run(write_new=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), st.out.view(torch.int16))
+    assert torch.equal(l1, st.lse_part)
+    live = torch.from_numpy(np.repeat(w.lengths > 0, w.qlen)).cuda()
+    assert not torch.isnan(st.out[live].float()).any()       # padded heads 96..127 (NaN) never read
+    assert (st.out[~live].view(torch.int16) == 0).all()
+
+
+def test_bad_index_poisons_not_faults(ops):
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("out-of-range cache index reads as NaN")
+    w = synth.make("tiny")
+    st = DeviceStep(w)
+    idx = st.indices.clone()
+    idx[3] = w.num_slots + 1000
+    st.indices = idx
+    st.attend(); st.merge()
+    torch.cuda.synchronize()
+    assert torch.isnan(st.latent[0, :w.heads].float()).all()     # request 0 uses the bad row
+    assert not torch.isnan(st.latent[1, :w.heads].float()).any()
+
+
+def test_empty_inputs_and_all_empty_requests(ops):
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("empty batch / all requests empty")
+    w = synth.make("tiny")
+    w.lengths[:] = 0
+    w.indptr[:] = 0
+    w.indices = w.indices[:1]  # never read: every request is empty
+    w.kv_rows = w.kv_rows[:0]
+    w.slot_mapping[:] = -1
+    st = DeviceStep(w)
+    st.o_part.fill_(float("nan"))
+    st.run()
+    torch.cuda.synchronize()
+    assert torch.isneginf(st.lse_part).all()
+    assert (st.latent.view(torch.int16) == 0).all()
+    assert (st.out.view(torch.int16) == 0).all()
+    # zero-size calls are no-ops
+    ops.kv_write(st.new_rows[:0, :512], st.new_rows[:0, 512:], st.slot_mapping[:0], st.kv_cache, 1.0)
+    ops.merge_lse(st.o_part[:, :0], st.lse_part[:, :0], st.latent[:0, :w.heads])
+
+
+def test_single_split_and_one_token(ops, oracle):
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce("num_splits=1, L=1 requests")
+    w = synth.make("batch", batch=3, len_range=(1, 1))
+    w.num_splits = 1
+    st = _run_step(ops, w, num_workers=4, split_min_tokens=1)
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache)
+    # L = 1: o equals kv_scale times the (only) value row
+    row = oracle.fp8_decode(cache[w.indices[0]])[:512] * w.kv_scale
+    got = oracle.bf16_decode(_np_bf16(st.latent)[0, 0])
+    assert np.abs(got - row).max() <= O_TOL
+
+
+# ------------------------------------------- full size, sampled (bench launch)
+
+@pytest.mark.parametrize("name", ["batch", "long", "spec_q8", "rank_share"])
+def test_full_size_sampled(ops, oracle, name):
+    """The bench configuration at full size; the oracle recomputes a few
+    sampled requests (their cache rows written by the oracle itself)."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"full-size sampled {name}")
+    w = synth.make(name)
+    st = DeviceStep(w)
+    st.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    nonempty = np.flatnonzero(w.lengths > 0)
+    n_sample = 1 if name == "long" else 2
+    sample = sorted(rng.choice(nonempty, size=min(n_sample, len(nonempty)), replace=False).tolist())
+    empty = np.flatnonzero(w.lengths == 0)
+    if len(empty):
+        sample.append(int(empty[0]))
+    cache = _oracle_cache(oracle, w, requests=sample)
+    gcache = st.kv_cache.cpu().numpy()
+    for r in sample:
+        rows = w.indices[w.indptr[r]:w.indptr[r + 1]]
+        assert np.array_equal(gcache[rows], cache[rows])
+    bounds, _ = oracle.split_bounds(w.indptr, w.num_splits, st.num_workers, st.split_min)
+    H = w.heads
+    # sub-problem of the sampled requests, with the full problem's split bounds
+    sub_ptr = np.concatenate([[0], np.cumsum([w.lengths[r] for r in sample])]).astype(np.int32)
+    sub_idx = np.concatenate([w.indices[w.indptr[r]:w.indptr[r + 1]] for r in sample]).astype(np.int32)
+    rows_t = np.concatenate([np.arange(r * w.qlen, (r + 1) * w.qlen) for r in sample])
+    q = np.ascontiguousarray(w.q[rows_t][:, :H])
+    o_ref, l_ref = oracle.decode_partial(q, cache, sub_ptr, sub_idx, bounds[sample], w.qlen, w.sm_scale,
+                                         w.kv_scale)
+    lse = st.lse_part.cpu().numpy()[:, rows_t].astype(np.float64)
+    o = oracle.bf16_decode(_np_bf16(st.o_part[:, torch.from_numpy(rows_t).cuda()]))
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(lse), ~fin)
+    assert np.abs(lse[fin] - l_ref[fin]).max(initial=0) <= LSE_TOL
+    assert np.abs(o[fin] - oracle.bf16_decode(oracle.bf16_round(o_ref))[fin]).max(initial=0) <= O_TOL
+    # merged latent of the sampled rows against the oracle's unsplit attention
+    one = np.stack([np.zeros(len(sample), np.int32), sub_ptr[1:] - sub_ptr[:-1]], 1).astype(np.int32)
+    o1, l1 = oracle.decode_partial(q, cache, sub_ptr, sub_idx, one, w.qlen, w.sm_scale, w.kv_scale)
+    lat = oracle.bf16_decode(_np_bf16(st.latent[torch.from_numpy(rows_t).cuda(), :H]))
+    f1 = np.isfinite(l1[0])
+    assert np.abs(lat[f1] - o1[0][f1]).max(initial=0) <= O_TOL
+    assert (lat[~f1] == 0).all()
+    # gated output rows: oracle value+gate on the GPU latent rows
+    latb = _np_bf16(st.latent[torch.from_numpy(rows_t).cuda()])
+    _, out_ref = oracle.value_gate(latb, w.gate[rows_t], w.lengths[sample], w.qlen, w_bf16=w.w_uv,
+                                   w_fp4=w.w_fp4, w_scale=w.w_scale)
+    got = oracle.bf16_decode(_np_bf16(st.out[torch.from_numpy(rows_t).cuda()]))
+    ref = oracle.bf16_decode(out_ref)
+    assert np.abs(got - ref).max() <= OUT_REL_TOL * max(np.abs(ref).max(), 1e-30)
