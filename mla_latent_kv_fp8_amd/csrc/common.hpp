@@ -84,6 +84,11 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// max that returns NaN if either operand is NaN
+__device__ __forceinline__ float nan_max(float a, float b) {
+  return (a != a || b != b) ? __builtin_nanf("") : fmaxf(a, b);
+}
+
 // ------------------------------------------------------------ split plan
 
 // The split partition of mla_decode_partial, shared by the device kernel

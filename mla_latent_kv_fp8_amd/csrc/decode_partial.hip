@@ -335,7 +335,9 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       const int m = m_lo + 16 * g + lr;
       if (m >= p.M) continue;
       const int t = r * p.qlen + m / p.heads, h = m % p.heads;
-      if (l > 0.0f) {
+      // l == 0: no visible token in this split.  A NaN l (NaN cache bytes)
+      // is written through, so it poisons the row instead of hiding it.
+      if (l != 0.0f) {
         const float inv = p.kv_scale / l;
         uint16_t* orow =
             p.o + k * p.os_s + (int64_t)t * p.os_r + (int64_t)h * p.os_h + 128 * wave + 4 * lg;
@@ -348,7 +350,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       }
       if (wave == 0 && lg == 0)
         p.lse[k * p.ls_s + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h] =
-            l > 0.0f ? (mref[g] + __log2f(l)) * kLn2 : -INFINITY;
+            l != 0.0f ? (mref[g] + __log2f(l)) * kLn2 : -INFINITY;
     }
     __syncthreads();
   }

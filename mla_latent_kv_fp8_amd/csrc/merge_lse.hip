@@ -16,11 +16,12 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
   const int64_t t = pair / heads, h = pair % heads;
   const float* lp = lse_part + t * ls_row + h * ls_head;
 
-  // max over splits (lanes stride over splits)
+  // max over splits (lanes stride over splits); a NaN LSE propagates so a
+  // poisoned split poisons the merged row
   float m = -INFINITY;
-  for (int k = lane; k < num_splits; k += 64) m = fmaxf(m, lp[k * ls_split]);
+  for (int k = lane; k < num_splits; k += 64) m = nan_max(m, lp[k * ls_split]);
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = wave_max_xor(m, s);
+  for (int s = 32; s >= 1; s >>= 1) m = nan_max(m, __shfl_xor(m, s));
 
   uint16_t* op = o + t * o_row + h * o_head + lane * 8;
   if (m == -INFINITY) {
