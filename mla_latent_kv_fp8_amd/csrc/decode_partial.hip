@@ -10,7 +10,10 @@
 //    All rows of a request share the same cache rows, so one staged tile
 //    feeds every head: QK and PV are dense MFMA contractions.
 //  * Per 64-token tile: the gathered fp8 rows (576 B each) are staged once in
-//    LDS, row-major with a 592-byte pitch and a 16-byte-chunk swizzle.
+//    LDS in swizzled 1 KB blocks of 16 tokens x 64 bytes, by asynchronous
+//    global->LDS loads into a double buffer (tile i+1 streams in while tile
+//    i is computed); the cache indices of a piece are staged in LDS first
+//    (2048 at a time).
 //  * QK on 16x16x32 bf16 MFMAs as S^T = K . Q^T: A = 16 tokens x 32 dims of
 //    the staged tile (fp8 -> bf16 in registers), B = Q^T held in registers
 //    for the whole piece.  Wave w owns token quarter w of every tile for all
@@ -20,7 +23,7 @@
 //    exchanged through LDS so every wave uses the same reference.
 //  * PV as O^T = V^T . P^T: wave w owns latent columns [128w, 128w+128).
 //    The A operand (8 tokens of one column) comes straight from the
-//    row-major tile with ds_read_b64_tr_b8; the B operand is P^T, written to
+//    staged tile with ds_read_b64_tr_b8; the B operand is P^T, written to
 //    LDS by the S-tile owners directly in MFMA operand order (the S^T
 //    accumulator layout gives each lane 4 consecutive tokens, so the PV
 //    contraction uses the matching token permutation).
@@ -28,8 +31,8 @@
 
 namespace mla {
 
-constexpr int NT = 64;      // tokens per tile
-constexpr int KP = 592;     // LDS bytes per staged token row (37 x 16 B)
+constexpr int NT = 64;             // tokens per tile
+constexpr int TILE_BYTES = 36864;  // one staged tile: 36 blocks of 1 KB
 constexpr float kLazy = 8.0f;  // rescale threshold, log2 units
 
 struct PartialArgs {
@@ -49,10 +52,16 @@ struct PartialArgs {
   int64_t ls_s, ls_r, ls_h;
 };
 
-// Position (in 16-B chunks) of chunk c of staged token t: the latent chunks
-// of tokens 16..31 (mod 32) are XOR-shifted by 4 so that the transposed V
-// reads (8 tokens {4G..4G+3, 16+4G..16+4G+3}) hit distinct banks.
-__device__ __forceinline__ int swz(int t, int c) { return c < 32 ? (c ^ (((t >> 4) & 1) << 2)) : c; }
+// LDS layout of a staged tile (64 tokens x 36 chunks of 16 B): block
+// (t/16, c/4) of 1 KB holds 16 tokens x 4 chunks; inside it, chunk c of
+// token t sits at 16-B slot 4*(t%16) + ((c%4) ^ h(t)).  With 32 banks the
+// QK fragment read (8 consecutive tokens, one chunk) and the transposed V
+// read (tokens {4G..4G+3} and {16+4G..16+4G+3}, one chunk) both hit 8
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int hsw(int t) { return ((t >> 1) & 3) ^ (((t >> 4) & 1) << 1); }
+__device__ __forceinline__ int tile_off(int t, int c) {
+  return 16 * (64 * (9 * (t >> 4) + (c >> 2)) + 4 * (t & 15) + ((c & 3) ^ hsw(t)));
+}
 
 // Query fragments of one 16-row group: K-step 2p uses dims 64p+16g..+7 and
 // K-step 2p+1 dims 64p+16g+8..+15 for lane group g (the same permutation
@@ -73,28 +82,63 @@ __device__ __forceinline__ void load_q(const PartialArgs& p, int r, int m, int l
 }
 
 // K fragment pair of (quarter qq, p): 16 bytes of token 16qq + lr at chunk
-// 4p + lg -> bf16 for K-steps 2p (lo) and 2p+1 (hi).
+// 4p + lg -> bf16 for K-steps 2p (lo) and 2p+1 (hi).  The 64 lanes read one
+// whole 1 KB block.
 __device__ __forceinline__ void load_k(const MLA_LDS uint8_t* kt, int qq, int pp, int lr, int lg,
                                        bf16x8& lo, bf16x8& hi) {
   const int t = 16 * qq + lr;
-  const u32x4 raw = *(const MLA_LDS u32x4*)(kt + t * KP + 16 * swz(t, 4 * pp + lg));
+  const u32x4 raw = *(const MLA_LDS u32x4*)(kt + tile_off(t, 4 * pp + lg));
   lo = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
   hi = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
 }
 
+// One direct global->LDS load of 16 bytes per lane: lane l's bytes land at
+// LDS byte address lds_base + 16*l.  Issued through inline assembly so that
+// the compiler does not make later LDS reads (of the other buffer) wait for
+// it; the kernel waits for these loads itself (vmcnt) before the barrier
+// that publishes a tile.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const uint8_t* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Issue the direct global->LDS loads of one 64-token tile.  Wave w loads the
+// 16 tokens of quarter w: load instruction cg fills block (w, cg), lane l
+// carrying token 16w + l/4, chunk 4cg + ((l%4) ^ h(t)).  Tokens past the
+// tile end and tokens with an invalid index load `safe_row` (masked, or
+// poisoned through the score).
+__device__ __forceinline__ void issue_tile(const uint8_t* kv, const MLA_LDS int32_t* idx_lds, int ntok,
+                                           int safe_row, MLA_LDS uint8_t* dst, int wave, int lane) {
+  const int t = 16 * wave + (lane >> 2);
+  int row = t < ntok ? idx_lds[t] : -1;
+  row = row < 0 ? safe_row : row;
+  const uint8_t* src = kv + (int64_t)row * MLA_D_QK + 16 * ((lane & 3) ^ hsw(t));
+  const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + 1024 * 9 * wave));
+#pragma unroll
+  for (int cg = 0; cg < 9; ++cg) lds_dma16(src + 64 * cg, d + 1024 * cg);
+}
+
+constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
+
 template <int NRG>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   constexpr int RB = 16 * NRG;
-  __shared__ __attribute__((aligned(16))) uint8_t kt_[NT * KP];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf_[2 * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * NRG * 64 * 8];
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
-  __shared__ int32_t tok_row[NT];
+  __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
   __shared__ int32_t red_i[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  MLA_LDS uint8_t* kt = (MLA_LDS uint8_t*)kt_;
+  MLA_LDS uint8_t* kbuf = (MLA_LDS uint8_t*)kbuf_;
+  MLA_LDS int32_t* idxl = (MLA_LDS int32_t*)idx;
 
   // ---- block -> (worker, row block); the row blocks of a worker share an
   // XCD (and its L2), workers interleave across the 8 XCDs
@@ -194,129 +238,153 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
     const int32_t* rows_r = p.indices + p.indptr[r];
 
-    for (int t0 = a; t0 < b; t0 += NT) {
-      const int ntok = min(NT, b - t0);
-      if (tid < NT) tok_row[tid] = tid < ntok ? rows_r[t0 + tid] : -1;
-      __syncthreads();
-      // stage 64 rows x 36 chunks of 16 B: thread -> token tid/4, chunks
-      // tid%4 + 4i; padding tokens are zero, bad indices read as fp8 NaN
+    for (int s0 = a; s0 < b; s0 += IDX_CAP) {
+      // ---- stage this segment's cache indices (invalid -> -1)
+      const int slen = min(IDX_CAP, b - s0);
+      __syncthreads();  // the previous segment's tiles are done with idx
       {
-        const int tt = tid >> 2, c0 = tid & 3;
-        const int row = tok_row[tt];
-        const bool live = tt < ntok, valid = (uint32_t)row < (uint64_t)p.num_slots;
-        const uint8_t* src = p.kv + (int64_t)(valid ? row : 0) * MLA_D_QK + 16 * c0;
-        MLA_LDS uint8_t* dst = kt + tt * KP + 16 * c0;
-        const int flip = ((tt >> 4) & 1) << 2;
+        int rowv[IDX_CAP / 256];
 #pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          u32x4 v = u32x4{0, 0, 0, 0};
-          if (live) {
-            if (valid)
-              v = *reinterpret_cast<const u32x4*>(src + 64 * i);
-            else
-              v = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-          }
-          // chunk c0 + 4i lands at position (c0 + 4i) ^ flip for the latent
-          const int pos = i < 8 ? 4 * (i ^ (flip >> 2)) : 4 * i;
-          *(MLA_LDS u32x4*)(dst + 16 * pos) = v;
+        for (int j = 0; j < IDX_CAP / 256; ++j) {
+          const int i = tid + 256 * j;
+          rowv[j] = i < slen ? rows_r[s0 + i] : -1;
+        }
+#pragma unroll
+        for (int j = 0; j < IDX_CAP / 256; ++j) {
+          const int i = tid + 256 * j;
+          if (i < slen) idx[i] = (uint32_t)rowv[j] < (uint64_t)p.num_slots ? rowv[j] : -1;
         }
       }
       __syncthreads();
+      int safe_row = 0;  // a valid row of this segment, for padding loads
+      {
+        int v = idx[0];
+        if (v < 0) {
+          for (int i = 1; i < slen; ++i)
+            if (idx[i] >= 0) { v = idx[i]; break; }
+        }
+        safe_row = v < 0 ? 0 : v;
+      }
+      const int ntiles = (slen + NT - 1) / NT;
+      issue_tile(p.kv, idxl, min(NT, slen), safe_row, kbuf, wave, lane);
 
-      // ---- QK: S^T (quarter `wave`, row group g) over the 576 dims
-      f32x4 S[NRG];
+      for (int it = 0; it < ntiles; ++it) {
+        const int t0 = s0 + NT * it;
+        MLA_LDS uint8_t* kt = kbuf + (it & 1) * TILE_BYTES;
+        wait_vm_all();                   // this wave's loads of tile `it` have landed
+        __syncthreads();                 // ... and every wave's; PV(it-1) is done
+        if (it + 1 < ntiles)
+          issue_tile(p.kv, idxl + NT * (it + 1), min(NT, slen - NT * (it + 1)), safe_row,
+                     kbuf + ((it + 1) & 1) * TILE_BYTES, wave, lane);
+
+        // ---- QK: S^T (quarter `wave`, row group g) over the 576 dims
+        f32x4 S[NRG];
 #pragma unroll
-      for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
+        for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
+        {
+          // K fragments read one step ahead of their use
+          const int tq = 16 * wave + lr;
+          u32x4 raw[2];
+          raw[0] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, lg));
 #pragma unroll
-      for (int pp = 0; pp < 9; ++pp) {
-        bf16x8 klo, khi;
-        load_k(kt, wave, pp, lr, lg, klo, khi);
+          for (int pp = 0; pp < 9; ++pp) {
+            if (pp + 1 < 9) raw[(pp + 1) & 1] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * (pp + 1) + lg));
+            const u32x4 cur = raw[pp & 1];
+            const bf16x8 klo = fp8x8_to_bf16x8(u32x2{cur[0], cur[1]});
+            const bf16x8 khi = fp8x8_to_bf16x8(u32x2{cur[2], cur[3]});
+#pragma unroll
+            for (int g = 0; g < NRG; ++g) {
+              S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
+              S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
+            }
+          }
+        }
+
+        // ---- scale, mask (an invalid index poisons with NaN), per-(row, quarter) max
+        const int32_t* ti = idx + NT * it + 16 * wave + 4 * lg;
+        bool bad[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad[e] = ti[e] < 0;
 #pragma unroll
         for (int g = 0; g < NRG; ++g) {
-          S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
-          S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = t0 + 16 * wave + 4 * lg + e;
+            float x = tok < lim[g] ? S[g][e] * p.c_log2 : -INFINITY;
+            if (bad[e] && tok < lim[g]) x = __builtin_nanf("");
+            S[g][e] = x;
+            mx = fmaxf(mx, x);
+          }
+          mx = wave_max_xor(mx, 16);
+          mx = wave_max_xor(mx, 32);
+          if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
         }
-      }
+        __syncthreads();
 
-      // ---- scale, mask, per-(row, quarter) max -> LDS
+        // ---- reference max update (identical in every wave), rescale
+        bool rescale = false;
+        float alpha[NRG];
 #pragma unroll
-      for (int g = 0; g < NRG; ++g) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = t0 + 16 * wave + 4 * lg + e;
-          const float x = tok < lim[g] ? S[g][e] * p.c_log2 : -INFINITY;
-          S[g][e] = x;
-          mx = fmaxf(mx, x);
+        for (int g = 0; g < NRG; ++g) {
+          const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+          const float mx = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
+          alpha[g] = 1.0f;
+          if (mx > mref[g] + kLazy) {
+            alpha[g] = __builtin_amdgcn_exp2f(mref[g] - mx);
+            mref[g] = mx;
+            rescale = true;
+          }
+          lsum[g] *= alpha[g];
         }
-        mx = wave_max_xor(mx, 16);
-        mx = wave_max_xor(mx, 32);
-        if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
-      }
-      __syncthreads();
+        if (__any(rescale)) {
+#pragma unroll
+          for (int d = 0; d < 8; ++d)
+#pragma unroll
+            for (int g = 0; g < NRG; ++g) O[d][g] *= alpha[g];
+        }
 
-      // ---- reference max update (identical in every wave), rescale
-      bool rescale = false;
-      float alpha[NRG];
+        // ---- P = exp2(x - mref) -> bf16 P^T fragments in LDS; row sums in f32
+        // (the PV contraction slot of lane-group G, element e is token
+        // 32*(quarter/2) + 16*(quarter%2) + 4G + e)
 #pragma unroll
-      for (int g = 0; g < NRG; ++g) {
-        const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-        const float mx = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-        alpha[g] = 1.0f;
-        if (mx > mref[g] + kLazy) {
-          alpha[g] = __builtin_amdgcn_exp2f(mref[g] - mx);
-          mref[g] = mx;
-          rescale = true;
+        for (int g = 0; g < NRG; ++g) {
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = S[g][e];
+            pv[e] = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - mref[g]);
+            lsum[g] += pv[e];
+          }
+          *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
+              u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
         }
-        lsum[g] *= alpha[g];
-      }
-      if (__any(rescale)) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d)
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) O[d][g] *= alpha[g];
-      }
+        __syncthreads();
 
-      // ---- P = exp2(x - mref) -> bf16 P^T fragments in LDS; row sums in f32
-      // (the PV contraction slot of lane-group G, element e is token
-      // 32*(quarter/2) + 16*(quarter%2) + 4G + e)
+        // ---- PV: O^T[128w + 16d .., rows] += V^T . P^T
 #pragma unroll
-      for (int g = 0; g < NRG; ++g) {
-        float pv[4];
+        for (int kap = 0; kap < 2; ++kap) {
+          // transposed V operand: source lane s of group G points at token
+          // slot (G, s/2), columns 16*chunk + 8*(s&1)
+          const int s2 = lr >> 1;
+          const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
+          const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
+          i32x2 vraw[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = S[g][e];
-          pv[e] = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - mref[g]);
-          lsum[g] += pv[e];
-        }
-        *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
-            u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-      }
-      __syncthreads();
-
-      // ---- PV: O^T[128w + 16d .., rows] += V^T . P^T
+          for (int d = 0; d < 8; ++d)
+            vraw[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
+          bf16x8 pf[NRG];
 #pragma unroll
-      for (int kap = 0; kap < 2; ++kap) {
-        // transposed V operand: source lane s of group G points at token
-        // slot (G, s/2), columns 16*chunk + 8*(s&1)
-        const int s2 = lr >> 1;
-        const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
-        const MLA_LDS uint8_t* vrow = kt + tt * KP + 8 * (lr & 1);
-        bf16x8 pf[NRG];
+          for (int g = 0; g < NRG; ++g)
+            pf[g] = *reinterpret_cast<const bf16x8*>(&pt[((kap * NRG + g) * 64 + lane) * 8]);
 #pragma unroll
-        for (int g = 0; g < NRG; ++g)
-          pf[g] = *reinterpret_cast<const bf16x8*>(&pt[((kap * NRG + g) * 64 + lane) * 8]);
+          for (int d = 0; d < 8; ++d) {
+            const bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[d][0], (uint32_t)vraw[d][1]});
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const int ch = 8 * wave + d;
-          const i32x2 raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (MLA_LDS i32x2*)(vrow + 16 * swz(tt, ch)));
-          const bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)raw[0], (uint32_t)raw[1]});
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[g], O[d][g]);
+            for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[g], O[d][g]);
+          }
         }
       }
-      __syncthreads();
     }
 
     // ---------------------------------------------------- piece epilogue
@@ -335,8 +403,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       const int m = m_lo + 16 * g + lr;
       if (m >= p.M) continue;
       const int t = r * p.qlen + m / p.heads, h = m % p.heads;
-      // l == 0: no visible token in this split.  A NaN l (NaN cache bytes)
-      // is written through, so it poisons the row instead of hiding it.
+      // l == 0: no visible token in this split.  A NaN l (NaN cache bytes or
+      // an invalid index) is written through, so it poisons the row.
       if (l != 0.0f) {
         const float inv = p.kv_scale / l;
         uint16_t* orow =
@@ -401,7 +469,7 @@ extern "C" int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64
     return MLA_ERR_INVALID;
   if (batch == 0) return MLA_OK;
   if (!q || !kv_cache || !kv_indptr || !kv_indices || !o_part || !lse_part) return MLA_ERR_INVALID;
-  if (num_slots < 0 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
+  if (num_slots < 1 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
   if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f)) return MLA_ERR_INVALID;
   // 16-byte query fragments, 8-byte partial stores, 16-byte cache rows
   if ((q_stride_row | q_stride_head) % 8 != 0 || ((uintptr_t)q) % 16 != 0) return MLA_ERR_UNSUPPORTED;

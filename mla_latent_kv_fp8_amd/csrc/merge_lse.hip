@@ -4,7 +4,9 @@
 
 namespace mla {
 
-// One wave per (row, head): lane l owns latent columns 8l..8l+7.
+// One wave per (row, head): lane l owns latent columns 8l..8l+7.  Lane k
+// holds split k's LSE (64 splits per pass); the finite splits are gathered
+// with a ballot and their rows loaded four at a time.
 __global__ void __launch_bounds__(256) merge_lse_kernel(
     const uint16_t* __restrict__ o_part, int64_t os_split, int64_t os_row, int64_t os_head,
     const float* __restrict__ lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
@@ -16,8 +18,7 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
   const int64_t t = pair / heads, h = pair % heads;
   const float* lp = lse_part + t * ls_row + h * ls_head;
 
-  // max over splits (lanes stride over splits); a NaN LSE propagates so a
-  // poisoned split poisons the merged row
+  // max over splits; a NaN LSE propagates so a poisoned split poisons the row
   float m = -INFINITY;
   for (int k = lane; k < num_splits; k += 64) m = nan_max(m, lp[k * ls_split]);
 #pragma unroll
@@ -29,10 +30,9 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
     if (lse != nullptr && lane == 0) lse[t * l_row + h * l_head] = -INFINITY;
     return;
   }
-  // sum of exp(lse_k - m), in split order within each lane, then a fixed tree
   float s = 0.0f;
   for (int k = lane; k < num_splits; k += 64) {
-    float l = lp[k * ls_split];
+    const float l = lp[k * ls_split];
     if (l != -INFINITY) s += expf(l - m);
   }
 #pragma unroll
@@ -41,15 +41,37 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const uint16_t* base = o_part + t * os_row + h * os_head + lane * 8;
-  for (int k = 0; k < num_splits; ++k) {
-    float l = lp[k * ls_split];  // uniform across the wave
-    if (l == -INFINITY) continue;
-    float w = expf(l - total);
-    u32x4 v = *reinterpret_cast<const u32x4*>(base + k * os_split);
+  for (int k0 = 0; k0 < num_splits; k0 += 64) {
+    const int k = k0 + lane;
+    const float l = k < num_splits ? lp[k * ls_split] : -INFINITY;
+    const float w = expf(l - total);  // 0 for empty splits, NaN if poisoned
+    uint64_t live = __ballot(l != -INFINITY);
+    while (live) {
+      int ks[4];
+      int n = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += w * __uint_as_float(v[e] << 16);
-      acc[2 * e + 1] += w * __uint_as_float(v[e] & 0xFFFF0000u);
+      for (int j = 0; j < 4; ++j) {
+        ks[j] = live ? __builtin_ctzll(live) : -1;
+        if (live) {
+          live &= live - 1;
+          ++n;
+        }
+      }
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ks[j] >= 0) v[j] = *reinterpret_cast<const u32x4*>(base + (int64_t)(k0 + ks[j]) * os_split);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ks[j] < 0) continue;
+        const float wj = __shfl(w, ks[j]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += wj * __uint_as_float(v[j][e] << 16);
+          acc[2 * e + 1] += wj * __uint_as_float(v[j][e] & 0xFFFF0000u);
+        }
+      }
+      (void)n;
     }
   }
   u32x4 out;

@@ -8,10 +8,12 @@ namespace mla {
 constexpr int VG_ROWS = 64;            // rows per workgroup
 constexpr int VG_PITCH = 512 + 8;      // LDS row pitch in bf16 (1040 B: conflict-free b128 reads)
 
-// Workgroup = (row block of 64, head).  Wave w computes outputs
-// v in [32w, 32w+32) for all 64 rows as C[v][t] = W[h][v][:] . latent[t][h][:]
-// on 16x16x32 bf16 MFMAs; the latent block is staged once in LDS and read as
-// the B operand, W fragments stream from global memory (each read once).
+// Workgroup = (row block of 64, head, half of the 128 outputs).  Wave w
+// computes outputs v in [64*half + 16w, +16) for all 64 rows as
+// C[v][t] = W[h][v][:] . latent[t][h][:] on 16x16x32 bf16 MFMAs.  Each
+// lane prefetches its W fragments for all 16 K-steps up front (every W
+// element is read once); the latent block is staged once in LDS and read as
+// the B operand.
 template <int FMT>
 __global__ void __launch_bounds__(256) value_gate_kernel(
     const uint16_t* __restrict__ latent, int64_t l_row, int64_t l_head, const void* __restrict__ w_uv,
@@ -22,74 +24,72 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.y;
   const int t0 = blockIdx.x * VG_ROWS;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int v = 64 * blockIdx.z + 16 * wave + lr;  // the A-operand row of this lane
+
+  // W fragments of all 16 K-steps (lane: output v, latents 32s + 8lg .. +7)
+  bf16x8 a[16];
+  if (FMT == MLA_W_BF16) {
+    const uint16_t* wp = reinterpret_cast<const uint16_t*>(w_uv) + h * w_head + v * w_v + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = *reinterpret_cast<const bf16x8*>(wp + 32 * s);
+  } else {
+    const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_uv) + h * w_head + v * w_v + 4 * lg;
+    const uint8_t* sp = w_scale + h * ws_head + v * ws_v;
+    uint32_t codes[16];
+    u32x4 sc4[4];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) codes[s] = *reinterpret_cast<const uint32_t*>(wp + 16 * s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc4[i] = u32x4{sp[4 * i], sp[4 * i + 1], sp[4 * i + 2], sp[4 * i + 3]};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) a[s] = fp4x8_to_bf16x8(codes[s], e8m0_to_f32(sc4[s >> 2][s & 3]));
+  }
 
   // stage the latent block: 64 rows x 64 chunks of 16 B
   for (int c = tid; c < VG_ROWS * 64; c += 256) {
     int r = c >> 6, part = c & 63;
-    u32x4 v = u32x4{0, 0, 0, 0};
+    u32x4 x = u32x4{0, 0, 0, 0};
     if (t0 + r < rows)
-      v = *reinterpret_cast<const u32x4*>(latent + (int64_t)(t0 + r) * l_row + h * l_head + part * 8);
-    *reinterpret_cast<u32x4*>(&lat[r * VG_PITCH + part * 8]) = v;
+      x = *reinterpret_cast<const u32x4*>(latent + (int64_t)(t0 + r) * l_row + h * l_head + part * 8);
+    *reinterpret_cast<u32x4*>(&lat[r * VG_PITCH + part * 8]) = x;
   }
   __syncthreads();
 
-  const int lr = lane & 15, lg = lane >> 4;
-  f32x4 acc[2][4];
+  f32x4 acc[4];
 #pragma unroll
-  for (int vb = 0; vb < 2; ++vb)
+  for (int rg = 0; rg < 4; ++rg) acc[rg] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) acc[vb][rg] = f32x4{0, 0, 0, 0};
-
-#pragma unroll 4
   for (int s = 0; s < 16; ++s) {
-    bf16x8 a[2];
-#pragma unroll
-    for (int vb = 0; vb < 2; ++vb) {
-      const int v = 32 * wave + 16 * vb + lr;
-      const int l0 = 32 * s + 8 * lg;
-      if (FMT == MLA_W_BF16) {
-        const uint16_t* wp = reinterpret_cast<const uint16_t*>(w_uv) + h * w_head + v * w_v + l0;
-        a[vb] = *reinterpret_cast<const bf16x8*>(wp);
-      } else {
-        const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_uv) + h * w_head + v * w_v + l0 / 2;
-        uint32_t codes = *reinterpret_cast<const uint32_t*>(wp);
-        float sc = e8m0_to_f32(w_scale[h * ws_head + v * ws_v + s]);
-        a[vb] = fp4x8_to_bf16x8(codes, sc);
-      }
-    }
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      bf16x8 b = *reinterpret_cast<const bf16x8*>(&lat[(16 * rg + lr) * VG_PITCH + 32 * s + 8 * lg]);
-#pragma unroll
-      for (int vb = 0; vb < 2; ++vb) acc[vb][rg] = mfma16(a[vb], b, acc[vb][rg]);
+      const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lat[(16 * rg + lr) * VG_PITCH + 32 * s + 8 * lg]);
+      acc[rg] = mfma16(a[s], b, acc[rg]);
     }
   }
 
-  // epilogue: lane holds v = 32w + 16vb + 4lg + i for row t = t0 + 16rg + lr
+  // epilogue: lane holds v = 64*half + 16w + 4lg + i for row t = t0 + 16rg + lr
 #pragma unroll
   for (int rg = 0; rg < 4; ++rg) {
     const int t = t0 + 16 * rg + lr;
     if (t >= rows) continue;
     const bool live = lengths[t / qlen] > 0;
+    const int col = h * MLA_D_V + 64 * blockIdx.z + 16 * wave + 4 * lg;
+    u32x2 res = u32x2{0, 0};
+    if (live) {
+      const u32x2 g = *reinterpret_cast<const u32x2*>(gate + t * g_row + col);
+      float o[4];
 #pragma unroll
-    for (int vb = 0; vb < 2; ++vb) {
-      const int col = h * MLA_D_V + 32 * wave + 16 * vb + 4 * lg;
-      u32x2 res = u32x2{0, 0};
-      if (live) {
-        u32x2 g = *reinterpret_cast<const u32x2*>(gate + t * g_row + col);
-        float o[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float val = bf16_bits_to_f32(f32_to_bf16_bits(acc[vb][rg][i]));
-          uint32_t gb = (i & 1) ? (g[i >> 1] >> 16) : (g[i >> 1] & 0xFFFFu);
-          float gl = bf16_bits_to_f32(gb);
-          float sig = 1.0f / (1.0f + expf(-gl));
-          o[i] = val * sig;
-        }
-        res = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      for (int i = 0; i < 4; ++i) {
+        const float val = bf16_bits_to_f32(f32_to_bf16_bits(acc[rg][i]));
+        const uint32_t gb = (i & 1) ? (g[i >> 1] >> 16) : (g[i >> 1] & 0xFFFFu);
+        const float gl = bf16_bits_to_f32(gb);
+        const float sig = 1.0f / (1.0f + expf(-gl));
+        o[i] = val * sig;
       }
-      *reinterpret_cast<u32x2*>(out + t * out_row + col) = res;
+      res = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
+    *reinterpret_cast<u32x2*>(out + t * out_row + col) = res;
   }
 }
 
@@ -108,7 +108,7 @@ extern "C" int mla_value_gate(const uint16_t* latent, int64_t l_row, int64_t l_h
   if ((l_row | l_head) % 8 != 0 || ((uintptr_t)latent) % 16 != 0) return MLA_ERR_UNSUPPORTED;
   if ((g_row | out_row) % 4 != 0 || (((uintptr_t)gate) | ((uintptr_t)out)) % 8 != 0)
     return MLA_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)((rows + mla::VG_ROWS - 1) / mla::VG_ROWS), (unsigned)heads);
+  dim3 grid((unsigned)((rows + mla::VG_ROWS - 1) / mla::VG_ROWS), (unsigned)heads, 2);
   hipStream_t s = (hipStream_t)stream;
   if (w_format == MLA_W_BF16) {
     if (w_v < MLA_D_LATENT || w_head < (int64_t)MLA_D_V * w_v) return MLA_ERR_INVALID;

@@ -82,19 +82,19 @@ SPECS = {
     "tiny": dict(batch=2, qlen=1, heads=16, heads_pad=16, fixed_lengths=[37, 64], kv_scale=1.0,
                  num_splits=2, split_min_tokens=1, num_workers=256, w_format="bf16", value_heads=16),
     "batch": dict(batch=64, qlen=1, heads=96, heads_pad=128, len_range=(1024, 8192), empty=4,
-                  kv_scale=0.05, num_splits=16, split_min_tokens=256, num_workers=256,
+                  kv_scale=0.05, num_splits=16, split_min_tokens=256, num_workers=128,
                   w_format="bf16", value_heads=96),
     "batch_8k": dict(batch=64, qlen=1, heads=96, heads_pad=128, fixed_lengths=[8192] * 64,
-                     kv_scale=0.05, num_splits=16, split_min_tokens=256, num_workers=256,
+                     kv_scale=0.05, num_splits=16, split_min_tokens=256, num_workers=128,
                      w_format="bf16", value_heads=96),
     "spec_q4": dict(batch=32, qlen=4, heads=96, heads_pad=96, len_range=(2048, 16384), kv_scale=0.05,
-                    num_splits=16, split_min_tokens=256, num_workers=64, w_format="bf16",
-                    value_heads=96, new_tokens=True),
-    "spec_q8": dict(batch=32, qlen=8, heads=96, heads_pad=96, len_range=(2048, 16384), kv_scale=0.05,
                     num_splits=16, split_min_tokens=256, num_workers=32, w_format="bf16",
                     value_heads=96, new_tokens=True),
+    "spec_q8": dict(batch=32, qlen=8, heads=96, heads_pad=96, len_range=(2048, 16384), kv_scale=0.05,
+                    num_splits=16, split_min_tokens=256, num_workers=16, w_format="bf16",
+                    value_heads=96, new_tokens=True),
     "long": dict(batch=16, qlen=1, heads=96, heads_pad=96, len_range=(32768, 131072), kv_scale=0.05,
-                 num_splits=64, split_min_tokens=256, num_workers=256, w_format="bf16",
+                 num_splits=64, split_min_tokens=256, num_workers=128, w_format="bf16",
                  value_heads=96),
     "rank_share": dict(batch=64, qlen=4, heads=12, heads_pad=12, len_range=(2048, 16384),
                        kv_scale=0.05, num_splits=16, split_min_tokens=256, num_workers=256,
