@@ -13,14 +13,20 @@
 //    LDS in swizzled 1 KB blocks of 16 tokens x 64 bytes, by asynchronous
 //    global->LDS loads into a double buffer (tile i+1 streams in while tile
 //    i is computed); the cache indices of a piece are staged in LDS first
-//    (2048 at a time).
+//    (2048 at a time), with the query rows, by the same direct loads.
 //  * QK on 16x16x32 bf16 MFMAs as S^T = K . Q^T: A = 16 tokens x 32 dims of
-//    the staged tile (fp8 -> bf16 in registers), B = Q^T held in registers
-//    for the whole piece.  Wave w owns token quarter w of every tile for all
-//    row groups, so each staged byte is converted to bf16 once per block.
-//  * Softmax: base-2 online softmax with a lazy reference max (rescale only
-//    when the running max grows by more than 2^8); per-tile row maxima are
-//    exchanged through LDS so every wave uses the same reference.
+//    the staged tile (fp8 -> bf16 in registers), B = Q^T, loaded once per
+//    piece into accumulation registers (the 48-row block keeps the last
+//    dims in LDS instead, so that O and Q fit the register file).  Wave w
+//    owns token quarter w of every tile for all row groups, so each staged
+//    byte is converted to bf16 once per block.
+//  * Softmax: base-2 online softmax against a lazy per-row reference: P =
+//    2^(x - ref) is kept in bf16 with f32 sums, so the reference only moves
+//    (and O is only rescaled, outside the hot loop) when a row's maximum
+//    exceeds it by more than 2^64; per-tile row maxima are exchanged through
+//    LDS so every wave uses the same reference.  Two barriers per tile: the
+//    max exchange, and "P^T written + next tile landed" (tiles are triple
+//    buffered, so the load of tile i+2 overlaps tiles i and i+1).
 //  * PV as O^T = V^T . P^T: wave w owns latent columns [128w, 128w+128).
 //    The A operand (8 tokens of one column) comes straight from the
 //    staged tile with ds_read_b64_tr_b8; the B operand is P^T, written to
@@ -33,7 +39,7 @@ namespace mla {
 
 constexpr int NT = 64;             // tokens per tile
 constexpr int TILE_BYTES = 36864;  // one staged tile: 36 blocks of 1 KB
-constexpr float kLazy = 8.0f;  // rescale threshold, log2 units
+constexpr float kLazy = 64.0f;  // rebase threshold, log2 units (P <= 2^64 in bf16 / f32 sums)
 
 struct PartialArgs {
   const uint16_t* q;
@@ -110,13 +116,13 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 // Issue the direct global->LDS loads of one 64-token tile.  Wave w loads the
 // 16 tokens of quarter w: load instruction cg fills block (w, cg), lane l
 // carrying token 16w + l/4, chunk 4cg + ((l%4) ^ h(t)).  Tokens past the
-// tile end and tokens with an invalid index load `safe_row` (masked, or
-// poisoned through the score).
-__device__ __forceinline__ void issue_tile(const uint8_t* kv, const MLA_LDS int32_t* idx_lds, int ntok,
-                                           int safe_row, MLA_LDS uint8_t* dst, int wave, int lane) {
+// tile end and tokens with an index outside [0, num_slots) load `safe_row`
+// (masked, or poisoned through the score).
+__device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots, const MLA_LDS int32_t* idx_lds,
+                                           int ntok, int safe_row, MLA_LDS uint8_t* dst, int wave, int lane) {
   const int t = 16 * wave + (lane >> 2);
   int row = t < ntok ? idx_lds[t] : -1;
-  row = row < 0 ? safe_row : row;
+  row = (uint32_t)row < (uint64_t)num_slots ? row : safe_row;
   const uint8_t* src = kv + (int64_t)row * MLA_D_QK + 16 * ((lane & 3) ^ hsw(t));
   const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + 1024 * 9 * wave));
 #pragma unroll
@@ -124,21 +130,152 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv, const MLA_LDS int3
 }
 
 constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
+constexpr int NBUF = 3;        // staged tiles in flight (triple buffering)
+#ifndef QREG3
+#define QREG3 4
+#endif
+// K-step pairs (64 dims each) of the query held in registers; the rest is
+// read from LDS every tile (only the 48-row block needs that, to fit O and
+// the query fragments in the 256 accumulation registers)
+template <int NRG> constexpr int qreg_pairs() { return NRG >= 3 ? QREG3 : 9; }
+
+// max over the 4 lane groups {l, l^16, l^32, l^48} with VALU lane swaps
+__device__ __forceinline__ float group_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Direct global->LDS staging of up to IDX_CAP cache indices (16 B = 4
+// indices per lane per load; chunks past n load chunk 0 again).
+__device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int32_t* idx_lds, int wave, int lane) {
+  const int nch = (n + 3) >> 2;
+  // rolled on purpose: the per-lane addresses are recomputed in place
+  // rather than hoisted (and spilled) across the piece loop
+#pragma unroll 1
+  for (int j = 0; j < IDX_CAP / 1024; ++j) {
+    const int blk = wave + 4 * j;  // 1 KB = 256 indices per load instruction
+    const int ch = 64 * blk + lane;
+    const int32_t* g = src + 4 * (ch < nch ? ch : 0);
+    const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(idx_lds + 256 * blk));
+    if (64 * blk < nch) lds_dma16(reinterpret_cast<const uint8_t*>(g), d);
+  }
+}
+
+// Query rows of one block plus the first index segment, all by direct
+// global->LDS loads.  With QR = qreg_pairs<NRG>(), dims [0, 64 QR) of row i
+// go to the staging area at qreg + i*qpitch_reg (read once into registers)
+// and dims [64 QR, 576) to the piece-resident area qlds + i*qpitch_lds.  A
+// row takes 8 chunks of 16 B per 64 dims plus one chunk of padding (which
+// staggers the rows over the LDS banks).
+template <int NRG> constexpr int qpitch_reg() { return 16 * (8 * qreg_pairs<NRG>() + 1); }
+template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 1); }
+
+template <int NRG>
+__device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
+                                                int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
+                                                MLA_LDS int32_t* idx_lds, int wave, int lane) {
+  constexpr int RB = 16 * NRG;
+  constexpr int QR = qreg_pairs<NRG>();
+  const uint16_t* q_base = p.q + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
+  auto src_of = [&](int row, int dim8) -> const uint16_t* {
+    const int m = m_lo + row;
+    if (row >= RB || m >= p.M) return q_base;  // dummy: the block's first row
+    const int jj = m / p.heads, h = m - p.heads * jj;
+    return p.q + (int64_t)(r * p.qlen + jj) * p.q_sr + (int64_t)h * p.q_sh + dim8;
+  };
+  // part 0: register dims
+  {
+    constexpr int W = 8 * QR + 1;
+    constexpr int NR = (RB * W + 63) / 64;
+#pragma unroll 1
+    for (int j0 = 0; j0 < NR; j0 += 4) {
+      const int j = j0 + wave;
+      if (j < NR) {
+        const int c = 64 * j + lane;
+        const int row = c / W, part = c - W * (c / W);
+        const uint16_t* g = part < W - 1 ? src_of(row, 8 * part) : q_base;
+        lds_dma16(reinterpret_cast<const uint8_t*>(g),
+                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qreg + 1024 * j)));
+      }
+    }
+  }
+  if constexpr (QR < 9) {
+    constexpr int W = 8 * (9 - QR) + 1;
+    constexpr int NL = (RB * W + 63) / 64;
+#pragma unroll 1
+    for (int j0 = 0; j0 < NL; j0 += 4) {
+      const int j = j0 + wave;
+      if (j < NL) {
+        const int c = 64 * j + lane;
+        const int row = c / W, part = c - W * (c / W);
+        const uint16_t* g = part < W - 1 ? src_of(row, 64 * QR + 8 * part) : q_base;
+        lds_dma16(reinterpret_cast<const uint8_t*>(g),
+                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qlds + 1024 * j)));
+      }
+    }
+  }
+  stage_idx(idx_src, nidx, idx_lds, wave, lane);
+}
+
+// PV of one tile: O^T[128w + 16d .., rows] += V^T . P^T over 2 K-steps of
+// 32 tokens.  The transposed V operand: source lane s of lane-group G points
+// at token slot (G, s/2), columns 16*chunk + 8*(s&1).  All reads are issued
+// before the conversions, and converting block d+1 overlaps the MFMAs of d.
+template <int NRG>
+__device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_t* pt, f32x4 (&O)[8][NRG],
+                                        int wave, int lane) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int kap = 0; kap < 2; ++kap) {
+    const int s2 = lr >> 1;
+    const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
+    const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
+    i32x2 vraw[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d)
+      vraw[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
+    bf16x8 pf[NRG];
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) pf[g] = *reinterpret_cast<const bf16x8*>(&pt[((kap * NRG + g) * 64 + lane) * 8]);
+    bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[0][0], (uint32_t)vraw[0][1]});
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      bf16x8 vn = vf;
+      if (d + 1 < 8) vn = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[d + 1][0], (uint32_t)vraw[d + 1][1]});
+#pragma unroll
+      for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[g], O[d][g]);
+      vf = vn;
+    }
+  }
+}
+
 
 template <int NRG>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   constexpr int RB = 16 * NRG;
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf_[2 * TILE_BYTES];
+  constexpr int QR = qreg_pairs<NRG>();
+  static_assert(((RB * (8 * QR + 1) + 63) / 64) * 1024 <= (NBUF - 1) * TILE_BYTES,
+                "query staging must fit in two tile buffers");
+  constexpr int QL_BYTES = QR < 9 ? ((RB * (8 * (9 - QR) + 1) + 63) / 64) * 1024 : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * NRG * 64 * 8];
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
+  __shared__ __attribute__((aligned(16))) uint8_t qlds_[QL_BYTES];
   __shared__ int32_t red_i[4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   MLA_LDS uint8_t* kbuf = (MLA_LDS uint8_t*)kbuf_;
   MLA_LDS int32_t* idxl = (MLA_LDS int32_t*)idx;
+  MLA_LDS uint8_t* qlds = (MLA_LDS uint8_t*)qlds_;
 
   // ---- block -> (worker, row block); the row blocks of a worker share an
   // XCD (and its L2), workers interleave across the 8 XCDs
@@ -155,34 +292,66 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
   }
 
-  // ---- the split partition: T, L_max -> chunk
+  // ---- the split partition: T, L_max -> chunk.  The request offsets are
+  // staged in LDS (the tile buffers are still free) when they fit.
+  const bool ip_lds = (int64_t)(p.batch + 1) * 4 <= (int64_t)NBUF * TILE_BYTES;
+  MLA_LDS int32_t* ipl = (MLA_LDS int32_t*)kbuf;
+  if (ip_lds) {
+    for (int i0 = 0; i0 <= p.batch; i0 += 1024) {
+      int v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + tid + 256 * j;
+        v[j] = i <= p.batch ? p.indptr[i] : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = i0 + tid + 256 * j;
+        if (i <= p.batch) ipl[i] = v[j];
+      }
+    }
+    __syncthreads();
+  }
+  auto ip = [&](int i) -> int { return ip_lds ? ipl[i] : p.indptr[i]; };
   int lmax = 0;
-  for (int r = tid; r < p.batch; r += 256) lmax = max(lmax, p.indptr[r + 1] - p.indptr[r]);
+  for (int r = tid; r < p.batch; r += 256) lmax = max(lmax, ip(r + 1) - ip(r));
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) lmax = max(lmax, __shfl_xor(lmax, s));
   if (lane == 0) red_i[wave] = lmax;
   __syncthreads();
   lmax = max(max(red_i[0], red_i[1]), max(red_i[2], red_i[3]));
-  const int base = p.indptr[0];
-  const int64_t T = (int64_t)p.indptr[p.batch] - base;
+  const int base = ip(0);
+  const int64_t T = (int64_t)ip(p.batch) - base;
   const int64_t chunk = split_chunk(T, lmax, p.num_splits, p.num_workers, p.split_min);
   const int64_t nunits = T > 0 ? (T + chunk - 1) / chunk : 1;
-  if (u >= nunits) return;
   const int64_t g0 = (int64_t)u * chunk;
   const int64_t g1 = g0 + chunk < T ? g0 + chunk : T;
   const bool last_unit = (u == nunits - 1);
   const int m_lo = rb * RB;  // first row (of the request's qlen*heads) of this block
 
-  // first request whose stream end is >= g0
-  int r;
-  {
+  // first request whose stream end is >= g0, and the requests this unit covers
+  int r = 0, r_end = 0;
+  if (u < nunits) {
     int lo = 0, hi = p.batch;
     while (lo < hi) {
       int mid = (lo + hi) >> 1;
-      if ((int64_t)p.indptr[mid + 1] - base >= g0) hi = mid; else lo = mid + 1;
+      if ((int64_t)ip(mid + 1) - base >= g0) hi = mid; else lo = mid + 1;
     }
     r = lo;
+    r_end = r;
+    while (r_end < p.batch) {
+      const int64_t P = (int64_t)ip(r_end) - base;
+      if (P >= g1 && !(last_unit && P == T)) break;
+      ++r_end;
+    }
   }
+  // (P, L) of the covered requests, read before the tile buffers are reused
+  constexpr int RMAX = 64;
+  __shared__ int32_t rP[RMAX + 1];
+  const int nreq = min(r_end - r, RMAX);
+  for (int i = tid; i <= nreq; i += 256) rP[i] = ip(r + i) - base;
+  __syncthreads();
+  if (u >= nunits) return;
 
   auto fill_neginf = [&](int req, int k_from) {
     // LSE = -inf for splits [k_from, num_splits) of every row of this block
@@ -195,10 +364,16 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
   };
 
-  for (; r < p.batch; ++r) {
-    const int64_t P = (int64_t)p.indptr[r] - base;
-    const int L = p.indptr[r + 1] - p.indptr[r];
-    if (P >= g1 && !(last_unit && P == T)) break;
+  for (int ri = 0; r < r_end; ++r, ++ri) {
+    int64_t P;
+    int L;
+    if (ri < nreq) {
+      P = rP[ri];
+      L = rP[ri + 1] - rP[ri];
+    } else {
+      P = (int64_t)p.indptr[r] - base;
+      L = p.indptr[r + 1] - p.indptr[r];
+    }
     if (L == 0) {
       const int64_t owner = P / chunk < nunits - 1 ? P / chunk : nunits - 1;
       if (owner == u) fill_neginf(r, 0);
@@ -214,16 +389,44 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
 
     // ---------------------------------------------------------- one piece
-    // wave w owns token quarter w of every tile, for all NRG row groups
-    bf16x8 qf[NRG][18];
+    const int32_t* rows_r = p.indices + p.indptr[r];
     int lim[NRG];  // visible tokens of row (g, lr), as an end in request tokens
+    int lim_min = b;
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
       const int m = m_lo + 16 * g + lr;
-      load_q(p, r, m, lg, qf[g]);
-      const int vis = m < p.M ? L - p.qlen + m / p.heads + 1 : 0;
+      // rows past M compute on a copy of a real row; their results are discarded
+      const int vis = m < p.M ? L - p.qlen + m / p.heads + 1 : b;
       lim[g] = min(b, vis);
+      lim_min = min(lim_min, lim[g]);
     }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, s));
+
+    // ---- stage the block's query rows and the first segment's cache
+    // indices in LDS with direct global->LDS loads (one round trip)
+    MLA_LDS uint8_t* qst = kbuf + TILE_BYTES;
+    stage_q_and_idx<NRG>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
+    wait_vm_all();
+    __syncthreads();
+    // query fragments for K-step pairs pp < QR: K-step 2pp uses dims
+    // 64pp+16lg..+7, 2pp+1 the next 8 (the K fragments use the same order)
+    bf16x8 qf[NRG][2 * QR];
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      const MLA_LDS uint8_t* src = qst + (16 * g + lr) * qpitch_reg<NRG>() + 32 * lg;
+#pragma unroll
+      for (int pp = 0; pp < QR; ++pp) {
+        qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src + 128 * pp);
+        qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src + 128 * pp + 16);
+      }
+    }
+    // keep the query fragments in AGPRs (they are only MFMA B operands), so
+    // the arch VGPRs hold the per-tile working set
+#pragma unroll
+    for (int g = 0; g < NRG; ++g)
+#pragma unroll
+      for (int ss = 0; ss < 2 * QR; ++ss) asm volatile("" : "+a"(qf[g][ss]));
 
     f32x4 O[8][NRG];
 #pragma unroll
@@ -236,154 +439,201 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       mref[g] = -INFINITY;
       lsum[g] = 0.0f;
     }
-    const int32_t* rows_r = p.indices + p.indptr[r];
 
     for (int s0 = a; s0 < b; s0 += IDX_CAP) {
-      // ---- stage this segment's cache indices (invalid -> -1)
       const int slen = min(IDX_CAP, b - s0);
-      __syncthreads();  // the previous segment's tiles are done with idx
-      {
-        int rowv[IDX_CAP / 256];
-#pragma unroll
-        for (int j = 0; j < IDX_CAP / 256; ++j) {
-          const int i = tid + 256 * j;
-          rowv[j] = i < slen ? rows_r[s0 + i] : -1;
-        }
-#pragma unroll
-        for (int j = 0; j < IDX_CAP / 256; ++j) {
-          const int i = tid + 256 * j;
-          if (i < slen) idx[i] = (uint32_t)rowv[j] < (uint64_t)p.num_slots ? rowv[j] : -1;
-        }
+      if (s0 != a) {
+        // ---- a later segment: stage its cache indices (invalid -> -1)
+        __syncthreads();  // the previous segment's tiles are done with idx / kbuf
+        stage_idx(rows_r + s0, slen, idxl, wave, lane);
+        wait_vm_all();
+        __syncthreads();
       }
-      __syncthreads();
       int safe_row = 0;  // a valid row of this segment, for padding loads
       {
         int v = idx[0];
-        if (v < 0) {
+        if ((uint32_t)v >= (uint64_t)p.num_slots) {
+          v = 0;
           for (int i = 1; i < slen; ++i)
-            if (idx[i] >= 0) { v = idx[i]; break; }
+            if ((uint32_t)idx[i] < (uint64_t)p.num_slots) { v = idx[i]; break; }
         }
-        safe_row = v < 0 ? 0 : v;
+        safe_row = v;
       }
       const int ntiles = (slen + NT - 1) / NT;
-      issue_tile(p.kv, idxl, min(NT, slen), safe_row, kbuf, wave, lane);
+      issue_tile(p.kv, p.num_slots, idxl, min(NT, slen), safe_row, kbuf, wave, lane);
+      __syncthreads();  // every wave has its query fragments: buffer 1 is free
+      if (ntiles > 1) issue_tile(p.kv, p.num_slots, idxl + NT, min(NT, slen - NT), safe_row, kbuf + TILE_BYTES, wave, lane);
+      if (ntiles > 1)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0's 9 loads (tile 1's may fly)
+      else
+        wait_vm_all();
+      __syncthreads();
 
-      for (int it = 0; it < ntiles; ++it) {
-        const int t0 = s0 + NT * it;
-        MLA_LDS uint8_t* kt = kbuf + (it & 1) * TILE_BYTES;
-        wait_vm_all();                   // this wave's loads of tile `it` have landed
-        __syncthreads();                 // ... and every wave's; PV(it-1) is done
-        if (it + 1 < ntiles)
-          issue_tile(p.kv, idxl + NT * (it + 1), min(NT, slen - NT * (it + 1)), safe_row,
-                     kbuf + ((it + 1) & 1) * TILE_BYTES, wave, lane);
-
-        // ---- QK: S^T (quarter `wave`, row group g) over the 576 dims
-        f32x4 S[NRG];
+      // One tile: QK + max exchange (phase A), then P + PV (phase B).  A row
+      // whose tile max exceeds its reference by more than 2^64 leaves the
+      // hot loop to rebase O (the only place O is rescaled).
+      int it = 0;
+      bool rebase = false;
+      f32x4 S[NRG];
+      float mnew[NRG];
+      while (true) {
+        for (; it < ntiles; ++it) {
+          const int t0 = s0 + NT * it;
+          const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
+          // ---- QK: S^T (quarter `wave`, row group g) over the 576 dims;
+          // all 9 fragment reads are issued first, and the conversion of
+          // step pp+1 overlaps the MFMAs of step pp
 #pragma unroll
-        for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
-        {
-          // K fragments read one step ahead of their use
-          const int tq = 16 * wave + lr;
-          u32x4 raw[2];
-          raw[0] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, lg));
+          for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
+          {
+            const int tq = 16 * wave + lr;
+            constexpr int RA = 3;  // fragment reads in flight
+            u32x4 raw[RA];
 #pragma unroll
-          for (int pp = 0; pp < 9; ++pp) {
-            if (pp + 1 < 9) raw[(pp + 1) & 1] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * (pp + 1) + lg));
-            const u32x4 cur = raw[pp & 1];
-            const bf16x8 klo = fp8x8_to_bf16x8(u32x2{cur[0], cur[1]});
-            const bf16x8 khi = fp8x8_to_bf16x8(u32x2{cur[2], cur[3]});
+            for (int pp = 0; pp < RA; ++pp) raw[pp] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * pp + lg));
+            bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
+            bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
 #pragma unroll
-            for (int g = 0; g < NRG; ++g) {
-              S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
-              S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
+            for (int pp = 0; pp < 9; ++pp) {
+              if (pp + RA < 9 + 1 && pp >= 1 && pp + RA - 1 < 9)
+                raw[(pp + RA - 1) % RA] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * (pp + RA - 1) + lg));
+              bf16x8 nlo = klo, nhi = khi;
+              if (pp + 1 < 9) {
+                nlo = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % RA][0], raw[(pp + 1) % RA][1]});
+                nhi = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % RA][2], raw[(pp + 1) % RA][3]});
+              }
+#pragma unroll
+              for (int g = 0; g < NRG; ++g) {
+                if (pp < QR) {
+                  S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
+                  S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
+                } else {
+                  const MLA_LDS uint8_t* qs = qlds + (16 * g + lr) * qpitch_lds<NRG>() + 128 * (pp - QR) + 32 * lg;
+                  S[g] = mfma16(klo, *(const MLA_LDS bf16x8*)qs, S[g]);
+                  S[g] = mfma16(khi, *(const MLA_LDS bf16x8*)(qs + 16), S[g]);
+                }
+              }
+              klo = nlo;
+              khi = nhi;
             }
           }
-        }
-
-        // ---- scale, mask (an invalid index poisons with NaN), per-(row, quarter) max
-        const int32_t* ti = idx + NT * it + 16 * wave + 4 * lg;
-        bool bad[4];
+          // ---- scale; mask only where a row's visible range or a bad
+          // index reaches into this quarter; per-(row, quarter) max -> LDS
+          {
+            const int tq0 = t0 + 16 * wave;
+            const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
+            const uint32_t ns = (uint32_t)p.num_slots;
+            const bool bad0 = (uint32_t)ids[0] >= ns, bad1 = (uint32_t)ids[1] >= ns;
+            const bool bad2 = (uint32_t)ids[2] >= ns, bad3 = (uint32_t)ids[3] >= ns;
+            const bool any_bad = __any(bad0 || bad1 || bad2 || bad3);
+            if (tq0 + 16 <= lim_min && !any_bad) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bad[e] = ti[e] < 0;
+              for (int g = 0; g < NRG; ++g) {
+                float mx = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < NRG; ++g) {
-          float mx = -INFINITY;
+                for (int e = 0; e < 4; ++e) {
+                  S[g][e] *= p.c_log2;
+                  mx = fmaxf(mx, S[g][e]);
+                }
+                mx = group_max4(mx);
+                if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
+              }
+            } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int tok = t0 + 16 * wave + 4 * lg + e;
-            float x = tok < lim[g] ? S[g][e] * p.c_log2 : -INFINITY;
-            if (bad[e] && tok < lim[g]) x = __builtin_nanf("");
-            S[g][e] = x;
-            mx = fmaxf(mx, x);
+              for (int g = 0; g < NRG; ++g) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int tok = tq0 + 4 * lg + e;
+                  float x = tok < lim[g] ? S[g][e] * p.c_log2 : -INFINITY;
+                  const bool bad = e == 0 ? bad0 : e == 1 ? bad1 : e == 2 ? bad2 : bad3;
+                  if (bad && tok < lim[g]) x = __builtin_nanf("");
+                  S[g][e] = x;
+                  mx = fmaxf(mx, x);
+                }
+                mx = group_max4(mx);
+                if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
+              }
+            }
           }
-          mx = wave_max_xor(mx, 16);
-          mx = wave_max_xor(mx, 32);
-          if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
-        }
-        __syncthreads();
-
-        // ---- reference max update (identical in every wave), rescale
-        bool rescale = false;
-        float alpha[NRG];
+          __syncthreads();  // B2: every quarter's maxima are in
+          bool need = false;
 #pragma unroll
-        for (int g = 0; g < NRG; ++g) {
-          const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-          const float mx = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-          alpha[g] = 1.0f;
-          if (mx > mref[g] + kLazy) {
-            alpha[g] = __builtin_amdgcn_exp2f(mref[g] - mx);
-            mref[g] = mx;
-            rescale = true;
+          for (int g = 0; g < NRG; ++g) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+            mnew[g] = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
+            // a row's first tile with a visible token sets its reference (O
+            // and the sum are still zero, so nothing needs rescaling)
+            if (mref[g] == -INFINITY) mref[g] = mnew[g];
+            need |= mnew[g] > mref[g] + kLazy;
           }
-          lsum[g] *= alpha[g];
+          // the same rows and data in every wave: the decision is block-uniform
+          if (__any(need)) {
+            rebase = true;
+            break;
+          }
+          // ---- phase B: P = exp2(x - mref) -> bf16 P^T fragments; row sums in f32
+#pragma unroll
+          for (int g = 0; g < NRG; ++g) {
+            const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
+            float pv[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
+              lsum[g] += pv[e];
+            }
+            *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
+                u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
+          }
+          if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
+          __syncthreads();                     // B3: P^T complete, tile it+1 visible
+          if (it + 2 < ntiles)
+            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
+                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+          pv_tile<NRG>(kt, pt, O, wave, lane);
         }
-        if (__any(rescale)) {
+        if (!rebase) break;
+        // ---- rare: rebase the rows whose maximum outgrew the reference,
+        // then finish tile `it` (phase B) and resume the hot loop
+        rebase = false;
+        {
+          float alpha[NRG];
+#pragma unroll
+          for (int g = 0; g < NRG; ++g) {
+            alpha[g] = 1.0f;
+            if (mnew[g] > mref[g] + kLazy) {
+              alpha[g] = __builtin_amdgcn_exp2f(mref[g] - mnew[g]);
+              mref[g] = mnew[g];
+            }
+            lsum[g] *= alpha[g];
+          }
 #pragma unroll
           for (int d = 0; d < 8; ++d)
 #pragma unroll
             for (int g = 0; g < NRG; ++g) O[d][g] *= alpha[g];
         }
-
-        // ---- P = exp2(x - mref) -> bf16 P^T fragments in LDS; row sums in f32
-        // (the PV contraction slot of lane-group G, element e is token
-        // 32*(quarter/2) + 16*(quarter%2) + 4G + e)
+        {
+          const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
 #pragma unroll
-        for (int g = 0; g < NRG; ++g) {
-          float pv[4];
+          for (int g = 0; g < NRG; ++g) {
+            const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
+            float pv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float x = S[g][e];
-            pv[e] = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - mref[g]);
-            lsum[g] += pv[e];
+            for (int e = 0; e < 4; ++e) {
+              pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
+              lsum[g] += pv[e];
+            }
+            *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
+                u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
           }
-          *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
-              u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+          if (it + 1 < ntiles) wait_vm_all();
+          __syncthreads();
+          if (it + 2 < ntiles)
+            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
+                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+          pv_tile<NRG>(kt, pt, O, wave, lane);
         }
-        __syncthreads();
-
-        // ---- PV: O^T[128w + 16d .., rows] += V^T . P^T
-#pragma unroll
-        for (int kap = 0; kap < 2; ++kap) {
-          // transposed V operand: source lane s of group G points at token
-          // slot (G, s/2), columns 16*chunk + 8*(s&1)
-          const int s2 = lr >> 1;
-          const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
-          const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
-          i32x2 vraw[8];
-#pragma unroll
-          for (int d = 0; d < 8; ++d)
-            vraw[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
-          bf16x8 pf[NRG];
-#pragma unroll
-          for (int g = 0; g < NRG; ++g)
-            pf[g] = *reinterpret_cast<const bf16x8*>(&pt[((kap * NRG + g) * 64 + lane) * 8]);
-#pragma unroll
-          for (int d = 0; d < 8; ++d) {
-            const bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[d][0], (uint32_t)vraw[d][1]});
-#pragma unroll
-            for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[g], O[d][g]);
-          }
-        }
+        ++it;
       }
     }
 
@@ -413,7 +663,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
         for (int d = 0; d < 8; ++d) {
           const f32x4 v = O[d][g];
           *reinterpret_cast<u32x2*>(orow + 16 * d) =
-              u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
+              u32x2{pk_bf16(v[0] * inv, v[1] * inv), pk_bf16(v[2] * inv, v[3] * inv)};
         }
       }
       if (wave == 0 && lg == 0)
