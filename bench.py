@@ -35,7 +35,24 @@ def parse():
     ap.add_argument("--config", default="batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
+                         "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        flush.zero_()
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
 
 
 def algorithmic(w):
@@ -47,6 +64,30 @@ def algorithmic(w):
         visible += int(np.maximum(L - w.qlen + j + 1, 0)[L > 0].sum())
     flops = 2176 * w.heads * visible
     return kv_bytes, flops
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the partial kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-probe calibration),
+    or None when that summary was taken on other kernel source."""
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "partial_kernel_%s_hbm_traffic.md" % config)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0] in ("traffic_bytes_per_launch", "source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k] = v.strip()
+    h = hashlib.sha256()
+    for src in ("decode_partial.hip", "common.hpp"):
+        with open(os.path.join(here, "mla_latent_kv_fp8_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    if fields.get("source_sha256") != h.hexdigest():
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(w, budget_s):
@@ -94,6 +135,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     import torch
 
     import mla_latent_kv_fp8_amd as m
@@ -179,7 +223,8 @@ def main():
                                                          w.num_workers, w.w_format),
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(args.config),
                      "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
                      "flops_per_launch": flops},
         "roofline_hbm": {"achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
