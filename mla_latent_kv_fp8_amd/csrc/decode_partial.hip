@@ -132,7 +132,10 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots,
 constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
 constexpr int NBUF = 3;        // staged tiles in flight (triple buffering)
 #ifndef QREG3
-#define QREG3 4
+#define QREG3 5
+#endif
+#ifndef QPIN3
+#define QPIN3 9
 #endif
 // K-step pairs (64 dims each) of the query held in registers; the rest is
 // read from LDS every tile (only the 48-row block needs that, to fit O and
@@ -223,38 +226,143 @@ __device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int
   stage_idx(idx_src, nidx, idx_lds, wave, lane);
 }
 
+// Scheduling hint for one unrolled step: NM groups of (1 MFMA, a share of NV
+// VALU instructions, a share of ND LDS reads), so the conversions and reads
+// issue in the shadow of the matrix pipe instead of around it.
+template <int NM, int NV, int ND, int I = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (I < NM) {
+    constexpr int nv = NV / NM + (I < NV % NM ? 1 : 0);
+    constexpr int nd = ND / NM + (I < ND % NM ? 1 : 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x002, nv, 0);
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+    interleave<NM, NV, ND, I + 1>();
+  }
+}
+
 // PV of one tile: O^T[128w + 16d .., rows] += V^T . P^T over 2 K-steps of
 // 32 tokens.  The transposed V operand: source lane s of lane-group G points
-// at token slot (G, s/2), columns 16*chunk + 8*(s&1).  All reads are issued
-// before the conversions, and converting block d+1 overlaps the MFMAs of d.
+// at token slot (G, s/2), columns 16*chunk + 8*(s&1).  read_v issues the 8
+// transposed reads of one K-step; pv_tile takes those of K-step 0 already
+// in flight (issued before the barrier that publishes P^T), issues K-step
+// 1's before K-step 0's MFMAs, and converts block d+1 while the MFMAs of d
+// run.
+__device__ __forceinline__ void read_v(const MLA_LDS uint8_t* kt, int kap, int wave, int lane, i32x2 (&v)[8]) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int s2 = lr >> 1;
+  const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
+  const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
+#pragma unroll
+  for (int d = 0; d < 8; ++d)
+    v[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
+}
+
 template <int NRG>
 __device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_t* pt, f32x4 (&O)[8][NRG],
-                                        int wave, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
+                                        const i32x2 (&v0)[8], int wave, int lane) {
+  bf16x8 pf[2][NRG];
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) pf[0][g] = *reinterpret_cast<const bf16x8*>(&pt[(g * 64 + lane) * 8]);
+  i32x2 v1[8];
+  read_v(kt, 1, wave, lane, v1);
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) pf[1][g] = *reinterpret_cast<const bf16x8*>(&pt[((NRG + g) * 64 + lane) * 8]);
 #pragma unroll
   for (int kap = 0; kap < 2; ++kap) {
-    const int s2 = lr >> 1;
-    const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
-    const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
-    i32x2 vraw[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      vraw[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
-    bf16x8 pf[NRG];
-#pragma unroll
-    for (int g = 0; g < NRG; ++g) pf[g] = *reinterpret_cast<const bf16x8*>(&pt[((kap * NRG + g) * 64 + lane) * 8]);
-    bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[0][0], (uint32_t)vraw[0][1]});
+    const i32x2(&vr)[8] = kap == 0 ? v0 : v1;
+    bf16x8 vf = fp8x8_to_bf16x8(u32x2{(uint32_t)vr[0][0], (uint32_t)vr[0][1]});
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       bf16x8 vn = vf;
-      if (d + 1 < 8) vn = fp8x8_to_bf16x8(u32x2{(uint32_t)vraw[d + 1][0], (uint32_t)vraw[d + 1][1]});
+      if (d + 1 < 8) vn = fp8x8_to_bf16x8(u32x2{(uint32_t)vr[d + 1][0], (uint32_t)vr[d + 1][1]});
 #pragma unroll
-      for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[g], O[d][g]);
+      for (int g = 0; g < NRG; ++g) O[d][g] = mfma16(vf, pf[kap][g], O[d][g]);
       vf = vn;
+      interleave<NRG, 4, 0>();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
+// QK of one tile for this wave's 16-token quarter and all row groups:
+// S[g] (16 tokens x 16 rows, C layout: tokens 4*(l/16).. of row l%16) =
+// K . Q^T over the 576 dims, as 9 K-step pairs.  Step pp uses chunk 4pp+lg
+// of token 16*wave+lr (block (wave, pp) of the staged tile); K reads run
+// two steps ahead of their conversion, LDS-resident query fragments one
+// step ahead of their MFMAs, and each step interleaves its MFMAs with the
+// conversions of the next step.
+template <int NRG, int QR>
+__device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 (&qf)[NRG][2 * QR],
+                                        const MLA_LDS uint8_t* qlds, int wave, int lane, f32x4 (&S)[NRG]) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
+  const MLA_LDS uint8_t* kq = kt + tile_off(16 * wave + lr, lg);
+  const MLA_LDS uint8_t* qq = qlds + lr * qpitch_lds<NRG>() + 32 * lg - 128 * QR;
+  u32x4 raw[3];
+  raw[0] = *(const MLA_LDS u32x4*)kq;
+  raw[1] = *(const MLA_LDS u32x4*)(kq + 1024);
+  bf16x8 ql[2][NRG][2];
+  if (QR == 0) {
+#pragma unroll
+    for (int g = 0; g < NRG; ++g)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ql[0][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 16 * h);
+  }
+  bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
+  bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
+#pragma unroll
+  for (int pp = 0; pp < 9; ++pp) {
+    if (pp + 2 < 9) raw[(pp + 2) % 3] = *(const MLA_LDS u32x4*)(kq + 1024 * (pp + 2));
+    if (pp + 1 >= QR && pp + 1 < 9) {
+#pragma unroll
+      for (int g = 0; g < NRG; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ql[(pp + 1) & 1][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + 1) + 16 * h);
+    }
+    bf16x8 nlo = klo, nhi = khi;
+    if (pp + 1 < 9) {
+      nlo = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % 3][0], raw[(pp + 1) % 3][1]});
+      nhi = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % 3][2], raw[(pp + 1) % 3][3]});
+    }
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      if (pp < QR) {
+        S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
+        S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
+      } else {
+        S[g] = mfma16(klo, ql[pp & 1][g][0], S[g]);
+        S[g] = mfma16(khi, ql[pp & 1][g][1], S[g]);
+      }
+    }
+    klo = nlo;
+    khi = nhi;
+    interleave<2 * NRG, 8, 3>();
+    __builtin_amdgcn_sched_barrier(0);  // keep the steps (and their read-ahead) in order
+  }
+}
+
+// P = 2^(S - ref) of this wave's quarter -> bf16 P^T fragments in LDS (in
+// the PV B-operand order), and the per-lane partial row sums.
+template <int NRG>
+__device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], const float (&mref)[NRG], uint16_t* ptb, int wave,
+                                       int lane, float (&ps)[NRG]) {
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) {
+    const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
+    float pv[4];
+    ps[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
+      ps[g] += pv[e];
+    }
+    *reinterpret_cast<u32x2*>(&ptb[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
+        u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
+  }
+}
 
 template <int NRG>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
@@ -264,7 +372,9 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
                 "query staging must fit in two tile buffers");
   constexpr int QL_BYTES = QR < 9 ? ((RB * (8 * (9 - QR) + 1) + 63) / 64) * 1024 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t pt[2 * NRG * 64 * 8];
+  constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
+  __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
+  __shared__ __attribute__((aligned(16))) int32_t redflag[8];          // rebase requests, by tile parity
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
@@ -426,24 +536,32 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
 #pragma unroll
     for (int g = 0; g < NRG; ++g)
 #pragma unroll
-      for (int ss = 0; ss < 2 * QR; ++ss) asm volatile("" : "+a"(qf[g][ss]));
+      for (int ss = 0; ss < 2 * (NRG >= 3 && QPIN3 < QR ? QPIN3 : QR); ++ss) asm volatile("" : "+a"(qf[g][ss]));
 
     f32x4 O[8][NRG];
+    float mref[NRG], lsum[NRG];
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) mref[g] = -INFINITY;
+
+    // The piece runs more than once only when a row's score outgrew its
+    // reference by more than 2^64: the reference then moves up and the
+    // piece restarts from its first token (O is never rescaled, so the hot
+    // loop touches O only through the MFMAs).
+    bool again = true;
+    bool restaged = false;  // the first segment's indices must be staged again
+    while (again) {
+    again = false;
 #pragma unroll
     for (int d = 0; d < 8; ++d)
 #pragma unroll
       for (int g = 0; g < NRG; ++g) O[d][g] = f32x4{0, 0, 0, 0};
-    float mref[NRG], lsum[NRG];
 #pragma unroll
-    for (int g = 0; g < NRG; ++g) {
-      mref[g] = -INFINITY;
-      lsum[g] = 0.0f;
-    }
+    for (int g = 0; g < NRG; ++g) lsum[g] = 0.0f;
 
-    for (int s0 = a; s0 < b; s0 += IDX_CAP) {
+    for (int s0 = a; s0 < b && !again; s0 += IDX_CAP) {
       const int slen = min(IDX_CAP, b - s0);
-      if (s0 != a) {
-        // ---- a later segment: stage its cache indices (invalid -> -1)
+      if (s0 != a || restaged) {
+        // ---- a later segment (or a restart): stage its cache indices
         __syncthreads();  // the previous segment's tiles are done with idx / kbuf
         stage_idx(rows_r + s0, slen, idxl, wave, lane);
         wait_vm_all();
@@ -469,56 +587,25 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
         wait_vm_all();
       __syncthreads();
 
-      // One tile: QK + max exchange (phase A), then P + PV (phase B).  A row
-      // whose tile max exceeds its reference by more than 2^64 leaves the
-      // hot loop to rebase O (the only place O is rescaled).
-      int it = 0;
-      bool rebase = false;
-      f32x4 S[NRG];
-      float mnew[NRG];
-      while (true) {
-        for (; it < ntiles; ++it) {
+      // One barrier per tile.  Each wave computes its quarter's scores and
+      // P against the shared reference optimistically and flags the rows
+      // that need a new one: a row's first finite maximum (its reference is
+      // set, nothing to rescale), or a maximum that outgrew the reference by
+      // more than 2^64 (rare: the loop is left to rescale O, the only place
+      // O is touched outside the MFMAs).  The flags are block-uniform after
+      // the barrier, since every wave reads the same exchanged maxima.
+      for (int it = 0; it < ntiles; ++it) {
+        f32x4 S[NRG];
+        float ps[NRG];
+        i32x2 v0[8];
+        {
           const int t0 = s0 + NT * it;
           const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
-          // ---- QK: S^T (quarter `wave`, row group g) over the 576 dims;
-          // all 9 fragment reads are issued first, and the conversion of
-          // step pp+1 overlaps the MFMAs of step pp
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
-          {
-            const int tq = 16 * wave + lr;
-            constexpr int RA = 3;  // fragment reads in flight
-            u32x4 raw[RA];
-#pragma unroll
-            for (int pp = 0; pp < RA; ++pp) raw[pp] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * pp + lg));
-            bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
-            bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
-#pragma unroll
-            for (int pp = 0; pp < 9; ++pp) {
-              if (pp + RA < 9 + 1 && pp >= 1 && pp + RA - 1 < 9)
-                raw[(pp + RA - 1) % RA] = *(const MLA_LDS u32x4*)(kt + tile_off(tq, 4 * (pp + RA - 1) + lg));
-              bf16x8 nlo = klo, nhi = khi;
-              if (pp + 1 < 9) {
-                nlo = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % RA][0], raw[(pp + 1) % RA][1]});
-                nhi = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % RA][2], raw[(pp + 1) % RA][3]});
-              }
-#pragma unroll
-              for (int g = 0; g < NRG; ++g) {
-                if (pp < QR) {
-                  S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
-                  S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
-                } else {
-                  const MLA_LDS uint8_t* qs = qlds + (16 * g + lr) * qpitch_lds<NRG>() + 128 * (pp - QR) + 32 * lg;
-                  S[g] = mfma16(klo, *(const MLA_LDS bf16x8*)qs, S[g]);
-                  S[g] = mfma16(khi, *(const MLA_LDS bf16x8*)(qs + 16), S[g]);
-                }
-              }
-              klo = nlo;
-              khi = nhi;
-            }
-          }
-          // ---- scale; mask only where a row's visible range or a bad
-          // index reaches into this quarter; per-(row, quarter) max -> LDS
+          uint16_t* ptb = pt + (it & 1) * PT_ELEMS;
+          qk_tile<NRG, QR>(kt, qf, qlds, wave, lane, S);
+          // ---- scale to log2 units; mask only where a row's visible range
+          // or a bad index reaches into this quarter; quarter maxima per row
+          float lm[NRG];
           {
             const int tq0 = t0 + 16 * wave;
             const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
@@ -535,8 +622,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
                   S[g][e] *= p.c_log2;
                   mx = fmaxf(mx, S[g][e]);
                 }
-                mx = group_max4(mx);
-                if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
+                lm[g] = group_max4(mx);
               }
             } else {
 #pragma unroll
@@ -551,91 +637,61 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
                   S[g][e] = x;
                   mx = fmaxf(mx, x);
                 }
-                mx = group_max4(mx);
-                if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = mx;
+                lm[g] = group_max4(mx);
               }
             }
           }
-          __syncthreads();  // B2: every quarter's maxima are in
-          bool need = false;
+          bool first = false, grow = false;
 #pragma unroll
           for (int g = 0; g < NRG; ++g) {
-            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-            mnew[g] = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-            // a row's first tile with a visible token sets its reference (O
-            // and the sum are still zero, so nothing needs rescaling)
-            if (mref[g] == -INFINITY) mref[g] = mnew[g];
-            need |= mnew[g] > mref[g] + kLazy;
+            first |= mref[g] == -INFINITY && lm[g] > -INFINITY;
+            grow |= mref[g] != -INFINITY && lm[g] > mref[g] + kLazy;
+            if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = lm[g];
           }
-          // the same rows and data in every wave: the decision is block-uniform
-          if (__any(need)) {
-            rebase = true;
+          if (lane == 0) redflag[4 * (it & 1) + wave] = (__any(grow) ? 2 : 0) | (__any(first) ? 1 : 0);
+          p_tile<NRG>(S, mref, ptb, wave, lane, ps);
+          read_v(kt, 0, wave, lane, v0);       // in flight across the barrier
+          if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
+          __syncthreads();                     // P^T, maxima and flags of tile it; tile it+1 visible
+          const i32x4 f4 = *(const MLA_LDS i32x4*)&redflag[4 * (it & 1)];
+          const int fl = f4[0] | f4[1] | f4[2] | f4[3];
+          if (it + 2 < ntiles)
+            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
+                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+          if (fl & 2) {
+            // rare: move the reference of the rows that outgrew it, restart
+#pragma unroll
+            for (int g = 0; g < NRG; ++g) {
+              const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+              const float mnew = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
+              if (mnew > mref[g] + kLazy) mref[g] = mnew;
+            }
+            again = true;
             break;
           }
-          // ---- phase B: P = exp2(x - mref) -> bf16 P^T fragments; row sums in f32
+          if (fl & 1) {
+            // first finite maxima: those rows take the exchanged maximum as
+            // their reference (O and the sum are still zero)
 #pragma unroll
-          for (int g = 0; g < NRG; ++g) {
-            const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
-            float pv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
-              lsum[g] += pv[e];
+            for (int g = 0; g < NRG; ++g) {
+              const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+              if (mref[g] == -INFINITY) mref[g] = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
             }
-            *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
-                u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
-          }
-          if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
-          __syncthreads();                     // B3: P^T complete, tile it+1 visible
-          if (it + 2 < ntiles)
-            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
-                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
-          pv_tile<NRG>(kt, pt, O, wave, lane);
-        }
-        if (!rebase) break;
-        // ---- rare: rebase the rows whose maximum outgrew the reference,
-        // then finish tile `it` (phase B) and resume the hot loop
-        rebase = false;
-        {
-          float alpha[NRG];
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) {
-            alpha[g] = 1.0f;
-            if (mnew[g] > mref[g] + kLazy) {
-              alpha[g] = __builtin_amdgcn_exp2f(mref[g] - mnew[g]);
-              mref[g] = mnew[g];
-            }
-            lsum[g] *= alpha[g];
+            p_tile<NRG>(S, mref, ptb, wave, lane, ps);
+            __syncthreads();  // the recomputed P^T is complete
           }
 #pragma unroll
-          for (int d = 0; d < 8; ++d)
-#pragma unroll
-            for (int g = 0; g < NRG; ++g) O[d][g] *= alpha[g];
+          for (int g = 0; g < NRG; ++g) lsum[g] += ps[g];
+          pv_tile<NRG>(kt, ptb, O, v0, wave, lane);
         }
-        {
-          const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) {
-            const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
-            float pv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
-              lsum[g] += pv[e];
-            }
-            *reinterpret_cast<u32x2*>(&pt[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
-                u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
-          }
-          if (it + 1 < ntiles) wait_vm_all();
-          __syncthreads();
-          if (it + 2 < ntiles)
-            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
-                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
-          pv_tile<NRG>(kt, pt, O, wave, lane);
-        }
-        ++it;
+      }
+      if (again) {
+        wait_vm_all();  // tile loads still in flight land before anything is restaged
+        __syncthreads();
+        restaged = true;
       }
     }
+    }  // while (again)
 
     // ---------------------------------------------------- piece epilogue
 #pragma unroll
