@@ -115,13 +115,18 @@ __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)
 
 // Issue the direct global->LDS loads of one 64-token tile.  Wave w loads the
 // 16 tokens of quarter w: load instruction cg fills block (w, cg), lane l
-// carrying token 16w + l/4, chunk 4cg + ((l%4) ^ h(t)).  Tokens past the
-// tile end and tokens with an index outside [0, num_slots) load `safe_row`
-// (masked, or poisoned through the score).
-__device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots, const MLA_LDS int32_t* idx_lds,
-                                           int ntok, int safe_row, MLA_LDS uint8_t* dst, int wave, int lane) {
+// carrying token 16w + l/4, chunk 4cg + ((l%4) ^ h(t)).  `row` is the cache
+// row of that token (tile_row); tokens past the tile end and tokens with an
+// index outside [0, num_slots) load `safe_row` (masked, or poisoned through
+// the score).
+__device__ __forceinline__ int tile_row(const MLA_LDS int32_t* idx_lds, int ntok, int wave, int lane) {
   const int t = 16 * wave + (lane >> 2);
-  int row = t < ntok ? idx_lds[t] : -1;
+  return t < ntok ? idx_lds[t] : -1;
+}
+
+__device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots, int row, int safe_row,
+                                           MLA_LDS uint8_t* dst, int wave, int lane) {
+  const int t = 16 * wave + (lane >> 2);
   row = (uint32_t)row < (uint64_t)num_slots ? row : safe_row;
   const uint8_t* src = kv + (int64_t)row * MLA_D_QK + 16 * ((lane & 3) ^ hsw(t));
   const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + 1024 * 9 * wave));
@@ -248,24 +253,40 @@ __device__ __forceinline__ void interleave() {
 // in flight (issued before the barrier that publishes P^T), issues K-step
 // 1's before K-step 0's MFMAs, and converts block d+1 while the MFMAs of d
 // run.
-__device__ __forceinline__ void read_v(const MLA_LDS uint8_t* kt, int kap, int wave, int lane, i32x2 (&v)[8]) {
+// Per-lane byte offsets of the transposed V reads within a tile, for
+// columns chunk 8*wave + j (j < 4) of K-step 0; chunk 8*wave + j + 4 is
+// 1 KB further and K-step 1 (tokens + 32) is 18 KB further, so 4 registers
+// address all 16 reads of a tile (the rest are immediate offsets).
+struct VOffsets {
+  int o[4];
+};
+__device__ __forceinline__ VOffsets v_offsets(int wave, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const int s2 = lr >> 1;
-  const int tt = 32 * kap + (s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4);
-  const MLA_LDS uint8_t* vrow = kt + 8 * (lr & 1);
+  const int tt = s2 < 4 ? 4 * lg + s2 : 16 + 4 * lg + s2 - 4;
+  VOffsets v;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v.o[j] = tile_off(tt, 8 * wave + j) + 8 * (lr & 1);
+  return v;
+}
+
+__device__ __forceinline__ void read_v(const MLA_LDS uint8_t* kt, int kap, const VOffsets& vo, i32x2 (&v)[8]) {
+  const MLA_LDS uint8_t* b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = kt + vo.o[j];
 #pragma unroll
   for (int d = 0; d < 8; ++d)
-    v[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(vrow + tile_off(tt, 8 * wave + d)));
+    v[d] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)(b[d & 3] + 1024 * (d >> 2) + 18432 * kap));
 }
 
 template <int NRG>
 __device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_t* pt, f32x4 (&O)[8][NRG],
-                                        const i32x2 (&v0)[8], int wave, int lane) {
+                                        const i32x2 (&v0)[8], const VOffsets& vo, int lane) {
   bf16x8 pf[2][NRG];
 #pragma unroll
   for (int g = 0; g < NRG; ++g) pf[0][g] = *reinterpret_cast<const bf16x8*>(&pt[(g * 64 + lane) * 8]);
   i32x2 v1[8];
-  read_v(kt, 1, wave, lane, v1);
+  read_v(kt, 1, vo, v1);
 #pragma unroll
   for (int g = 0; g < NRG; ++g) pf[1][g] = *reinterpret_cast<const bf16x8*>(&pt[((NRG + g) * 64 + lane) * 8]);
 #pragma unroll
@@ -344,21 +365,18 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
   }
 }
 
-// P = 2^(S - ref) of this wave's quarter -> bf16 P^T fragments in LDS (in
-// the PV B-operand order), and the per-lane partial row sums.
+// P = 2^(c*S - ref) of this wave's quarter (S in raw score units, nmb =
+// -ref) -> bf16 P^T fragments in LDS (in the PV B-operand order), and the
+// per-lane partial row sums.
 template <int NRG>
-__device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], const float (&mref)[NRG], uint16_t* ptb, int wave,
-                                       int lane, float (&ps)[NRG]) {
+__device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const float (&nmb)[NRG], uint16_t* ptb,
+                                       int wave, int lane, float (&ps)[NRG]) {
 #pragma unroll
   for (int g = 0; g < NRG; ++g) {
-    const float mb = mref[g] == -INFINITY ? 0.0f : mref[g];
     float pv[4];
-    ps[g] = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pv[e] = __builtin_amdgcn_exp2f(S[g][e] - mb);
-      ps[g] += pv[e];
-    }
+    for (int e = 0; e < 4; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(S[g][e], c, nmb[g]));
+    ps[g] = (pv[0] + pv[1]) + (pv[2] + pv[3]);
     *reinterpret_cast<u32x2*>(&ptb[(((wave >> 1) * NRG + g) * 64 + lane) * 8 + 4 * (wave & 1)]) =
         u32x2{pk_bf16(pv[0], pv[1]), pk_bf16(pv[2], pv[3])};
   }
@@ -386,6 +404,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   MLA_LDS uint8_t* kbuf = (MLA_LDS uint8_t*)kbuf_;
   MLA_LDS int32_t* idxl = (MLA_LDS int32_t*)idx;
   MLA_LDS uint8_t* qlds = (MLA_LDS uint8_t*)qlds_;
+  const VOffsets vo = v_offsets(wave, lane);
 
   // ---- block -> (worker, row block); the row blocks of a worker share an
   // XCD (and its L2), workers interleave across the 8 XCDs
@@ -512,6 +531,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, s));
+    lim_min = __builtin_amdgcn_readfirstlane(lim_min);  // wave-uniform: keep the mask test scalar
 
     // ---- stage the block's query rows and the first segment's cache
     // indices in LDS with direct global->LDS loads (one round trip)
@@ -539,9 +559,15 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       for (int ss = 0; ss < 2 * (NRG >= 3 && QPIN3 < QR ? QPIN3 : QR); ++ss) asm volatile("" : "+a"(qf[g][ss]));
 
     f32x4 O[8][NRG];
-    float mref[NRG], lsum[NRG];
+    // per row: reference (log2 units), raw-score threshold of the flag, -ref
+    float mref[NRG], thr[NRG], nmb[NRG], lsum[NRG];
+    const float inv_c = 1.0f / p.c_log2;
 #pragma unroll
-    for (int g = 0; g < NRG; ++g) mref[g] = -INFINITY;
+    for (int g = 0; g < NRG; ++g) {
+      mref[g] = -INFINITY;
+      thr[g] = -INFINITY;
+      nmb[g] = 0.0f;
+    }
 
     // The piece runs more than once only when a row's score outgrew its
     // reference by more than 2^64: the reference then moves up and the
@@ -578,9 +604,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
         safe_row = v;
       }
       const int ntiles = (slen + NT - 1) / NT;
-      issue_tile(p.kv, p.num_slots, idxl, min(NT, slen), safe_row, kbuf, wave, lane);
+      issue_tile(p.kv, p.num_slots, tile_row(idxl, min(NT, slen), wave, lane), safe_row, kbuf, wave, lane);
       __syncthreads();  // every wave has its query fragments: buffer 1 is free
-      if (ntiles > 1) issue_tile(p.kv, p.num_slots, idxl + NT, min(NT, slen - NT), safe_row, kbuf + TILE_BYTES, wave, lane);
+      if (ntiles > 1)
+        issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
+                   kbuf + TILE_BYTES, wave, lane);
       if (ntiles > 1)
         asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0's 9 loads (tile 1's may fly)
       else
@@ -595,95 +623,83 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       // O is touched outside the MFMAs).  The flags are block-uniform after
       // the barrier, since every wave reads the same exchanged maxima.
       for (int it = 0; it < ntiles; ++it) {
+        const int t0 = s0 + NT * it;
+        const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
+        uint16_t* ptb = pt + (it & 1) * PT_ELEMS;
+        // indices for this tile's mask and tile it+2's loads, read ahead of QK
+        const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
+        const int nrow = it + 2 < ntiles ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
         f32x4 S[NRG];
-        float ps[NRG];
-        i32x2 v0[8];
+        qk_tile<NRG, QR>(kt, qf, qlds, wave, lane, S);
+        // ---- mask (raw score units) only where a row's visible range or a
+        // bad index reaches into this quarter
         {
-          const int t0 = s0 + NT * it;
-          const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
-          uint16_t* ptb = pt + (it & 1) * PT_ELEMS;
-          qk_tile<NRG, QR>(kt, qf, qlds, wave, lane, S);
-          // ---- scale to log2 units; mask only where a row's visible range
-          // or a bad index reaches into this quarter; quarter maxima per row
-          float lm[NRG];
-          {
-            const int tq0 = t0 + 16 * wave;
-            const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
-            const uint32_t ns = (uint32_t)p.num_slots;
-            const bool bad0 = (uint32_t)ids[0] >= ns, bad1 = (uint32_t)ids[1] >= ns;
-            const bool bad2 = (uint32_t)ids[2] >= ns, bad3 = (uint32_t)ids[3] >= ns;
-            const bool any_bad = __any(bad0 || bad1 || bad2 || bad3);
-            if (tq0 + 16 <= lim_min && !any_bad) {
+          const int tq0 = t0 + 16 * wave;
+          const uint32_t ns = (uint32_t)p.num_slots;
+          const bool bad0 = (uint32_t)ids[0] >= ns, bad1 = (uint32_t)ids[1] >= ns;
+          const bool bad2 = (uint32_t)ids[2] >= ns, bad3 = (uint32_t)ids[3] >= ns;
+          const bool any_bad = __any(bad0 || bad1 || bad2 || bad3);
+          if (!(tq0 + 16 <= lim_min && !any_bad)) {
 #pragma unroll
-              for (int g = 0; g < NRG; ++g) {
-                float mx = -INFINITY;
+            for (int g = 0; g < NRG; ++g)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  S[g][e] *= p.c_log2;
-                  mx = fmaxf(mx, S[g][e]);
-                }
-                lm[g] = group_max4(mx);
+              for (int e = 0; e < 4; ++e) {
+                const int tok = tq0 + 4 * lg + e;
+                const bool bad = e == 0 ? bad0 : e == 1 ? bad1 : e == 2 ? bad2 : bad3;
+                S[g][e] = tok < lim[g] ? (bad ? __builtin_nanf("") : S[g][e]) : -INFINITY;
               }
-            } else {
-#pragma unroll
-              for (int g = 0; g < NRG; ++g) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const int tok = tq0 + 4 * lg + e;
-                  float x = tok < lim[g] ? S[g][e] * p.c_log2 : -INFINITY;
-                  const bool bad = e == 0 ? bad0 : e == 1 ? bad1 : e == 2 ? bad2 : bad3;
-                  if (bad && tok < lim[g]) x = __builtin_nanf("");
-                  S[g][e] = x;
-                  mx = fmaxf(mx, x);
-                }
-                lm[g] = group_max4(mx);
-              }
-            }
           }
-          bool first = false, grow = false;
+        }
+        // ---- flag: a score of this quarter above its row's threshold (the
+        // reference plus 2^64, or any finite score while there is none)
+        bool need = false;
+#pragma unroll
+        for (int g = 0; g < NRG; ++g)
+          need |= fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3])) > thr[g];
+        if (lane == 0) redflag[4 * (it & 1) + wave] = __any(need) ? 1 : 0;
+        float ps[NRG];
+        p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
+        i32x2 v0[8];
+        read_v(kt, 0, vo, v0);               // in flight across the barrier
+        if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
+        __syncthreads();                     // P^T and flags of tile it; tile it+1 visible
+        const i32x4 f4 = *(const MLA_LDS i32x4*)&redflag[4 * (it & 1)];
+        if (it + 2 < ntiles)
+          issue_tile(p.kv, p.num_slots, nrow, safe_row, kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+        if (__builtin_amdgcn_readfirstlane(f4[0] | f4[1] | f4[2] | f4[3])) {
+          // ---- rare (a piece's first tile): exchange the quarter maxima;
+          // rows without a reference take theirs, rows that outgrew theirs
+          // by more than 2^64 restart the piece with the new one
 #pragma unroll
           for (int g = 0; g < NRG; ++g) {
-            first |= mref[g] == -INFINITY && lm[g] > -INFINITY;
-            grow |= mref[g] != -INFINITY && lm[g] > mref[g] + kLazy;
-            if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = lm[g];
+            const float lm = group_max4(fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3]))) * p.c_log2;
+            if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = lm;
           }
-          if (lane == 0) redflag[4 * (it & 1) + wave] = (__any(grow) ? 2 : 0) | (__any(first) ? 1 : 0);
-          p_tile<NRG>(S, mref, ptb, wave, lane, ps);
-          read_v(kt, 0, wave, lane, v0);       // in flight across the barrier
-          if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
-          __syncthreads();                     // P^T, maxima and flags of tile it; tile it+1 visible
-          const i32x4 f4 = *(const MLA_LDS i32x4*)&redflag[4 * (it & 1)];
-          const int fl = f4[0] | f4[1] | f4[2] | f4[3];
-          if (it + 2 < ntiles)
-            issue_tile(p.kv, p.num_slots, idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), safe_row,
-                       kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
-          if (fl & 2) {
-            // rare: move the reference of the rows that outgrew it, restart
+          __syncthreads();
+          bool grow = false;
 #pragma unroll
-            for (int g = 0; g < NRG; ++g) {
-              const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-              const float mnew = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-              if (mnew > mref[g] + kLazy) mref[g] = mnew;
+          for (int g = 0; g < NRG; ++g) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+            const float mnew = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
+            if (mref[g] == -INFINITY) {
+              mref[g] = mnew;  // stays -inf while the row has seen no finite score
+            } else if (mnew > mref[g] + kLazy) {
+              mref[g] = mnew;
+              grow = true;
             }
+            thr[g] = mref[g] == -INFINITY ? -INFINITY : (mref[g] + kLazy) * inv_c;
+            nmb[g] = mref[g] == -INFINITY ? 0.0f : -mref[g];
+          }
+          if (__any(grow)) {  // the same maxima in every wave: block-uniform
             again = true;
             break;
           }
-          if (fl & 1) {
-            // first finite maxima: those rows take the exchanged maximum as
-            // their reference (O and the sum are still zero)
-#pragma unroll
-            for (int g = 0; g < NRG; ++g) {
-              const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-              if (mref[g] == -INFINITY) mref[g] = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-            }
-            p_tile<NRG>(S, mref, ptb, wave, lane, ps);
-            __syncthreads();  // the recomputed P^T is complete
-          }
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) lsum[g] += ps[g];
-          pv_tile<NRG>(kt, ptb, O, v0, wave, lane);
+          p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
+          __syncthreads();  // the recomputed P^T is complete
         }
+#pragma unroll
+        for (int g = 0; g < NRG; ++g) lsum[g] += ps[g];
+        pv_tile<NRG>(kt, ptb, O, v0, vo, lane);
       }
       if (again) {
         wait_vm_all();  // tile loads still in flight land before anything is restaged
