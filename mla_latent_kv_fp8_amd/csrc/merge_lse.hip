@@ -4,6 +4,32 @@
 
 namespace mla {
 
+// Reductions over the 64 lanes of a wave without LDS traffic: rotations
+// within each 16-lane row (DPP), then the swaps across rows.
+__device__ __forceinline__ float dpp_ror(float x, int n) {
+  const int v = __float_as_int(x);
+  int r;
+  switch (n) {
+    case 8: r = __builtin_amdgcn_update_dpp(v, v, 0x128, 0xF, 0xF, false); break;
+    case 4: r = __builtin_amdgcn_update_dpp(v, v, 0x124, 0xF, 0xF, false); break;
+    case 2: r = __builtin_amdgcn_update_dpp(v, v, 0x122, 0xF, 0xF, false); break;
+    default: r = __builtin_amdgcn_update_dpp(v, v, 0x121, 0xF, 0xF, false); break;
+  }
+  return __int_as_float(r);
+}
+
+template <typename F>
+__device__ __forceinline__ float wave_reduce(float x, F op) {
+  x = op(x, dpp_ror(x, 8));
+  x = op(x, dpp_ror(x, 4));
+  x = op(x, dpp_ror(x, 2));
+  x = op(x, dpp_ror(x, 1));
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // One wave per (row, head): lane l owns latent columns 8l..8l+7.  Lane k
 // holds split k's LSE (64 splits per pass); the finite splits are gathered
 // with a ballot and their rows loaded four at a time.
@@ -21,8 +47,7 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
   // max over splits; a NaN LSE propagates so a poisoned split poisons the row
   float m = -INFINITY;
   for (int k = lane; k < num_splits; k += 64) m = nan_max(m, lp[k * ls_split]);
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = nan_max(m, __shfl_xor(m, s));
+  m = wave_reduce(m, [](float a, float b) { return nan_max(a, b); });
 
   uint16_t* op = o + t * o_row + h * o_head + lane * 8;
   if (m == -INFINITY) {
@@ -35,8 +60,7 @@ __global__ void __launch_bounds__(256) merge_lse_kernel(
     const float l = lp[k * ls_split];
     if (l != -INFINITY) s += expf(l - m);
   }
-#pragma unroll
-  for (int sh = 32; sh >= 1; sh >>= 1) s += __shfl_xor(s, sh);
+  s = wave_reduce(s, [](float a, float b) { return a + b; });
   const float total = m + logf(s);
 
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};

@@ -46,13 +46,32 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
     for (int s = 0; s < 16; ++s) a[s] = fp4x8_to_bf16x8(codes[s], e8m0_to_f32(sc4[s >> 2][s & 3]));
   }
 
-  // stage the latent block: 64 rows x 64 chunks of 16 B
-  for (int c = tid; c < VG_ROWS * 64; c += 256) {
-    int r = c >> 6, part = c & 63;
-    u32x4 x = u32x4{0, 0, 0, 0};
-    if (t0 + r < rows)
-      x = *reinterpret_cast<const u32x4*>(latent + (int64_t)(t0 + r) * l_row + h * l_head + part * 8);
-    *reinterpret_cast<u32x4*>(&lat[r * VG_PITCH + part * 8]) = x;
+  // stage the latent block (64 rows x 64 chunks of 16 B) with all loads in
+  // flight at once; the epilogue's gate values and row lengths are fetched
+  // here too, so their latency hides behind the staging and the MFMAs
+  {
+    u32x4 x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = tid + 256 * i, r = c >> 6, part = c & 63;
+      x[i] = u32x4{0, 0, 0, 0};
+      if (t0 + r < rows)
+        x[i] = *reinterpret_cast<const u32x4*>(latent + (int64_t)(t0 + r) * l_row + h * l_head + part * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = tid + 256 * i, r = c >> 6, part = c & 63;
+      *reinterpret_cast<u32x4*>(&lat[r * VG_PITCH + part * 8]) = x[i];
+    }
+  }
+  const int col = h * MLA_D_V + 64 * blockIdx.z + 16 * wave + 4 * lg;
+  u32x2 gv[4];
+  int len[4];
+#pragma unroll
+  for (int rg = 0; rg < 4; ++rg) {
+    const int t = min(t0 + 16 * rg + lr, rows - 1);  // rows past the end: a real row, not stored
+    len[rg] = lengths[t / qlen];
+    gv[rg] = *reinterpret_cast<const u32x2*>(gate + t * g_row + col);
   }
   __syncthreads();
 
@@ -73,16 +92,13 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
   for (int rg = 0; rg < 4; ++rg) {
     const int t = t0 + 16 * rg + lr;
     if (t >= rows) continue;
-    const bool live = lengths[t / qlen] > 0;
-    const int col = h * MLA_D_V + 64 * blockIdx.z + 16 * wave + 4 * lg;
     u32x2 res = u32x2{0, 0};
-    if (live) {
-      const u32x2 g = *reinterpret_cast<const u32x2*>(gate + t * g_row + col);
+    if (len[rg] > 0) {
       float o[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float val = bf16_bits_to_f32(f32_to_bf16_bits(acc[rg][i]));
-        const uint32_t gb = (i & 1) ? (g[i >> 1] >> 16) : (g[i >> 1] & 0xFFFFu);
+        const uint32_t gb = (i & 1) ? (gv[rg][i >> 1] >> 16) : (gv[rg][i >> 1] & 0xFFFFu);
         const float gl = bf16_bits_to_f32(gb);
         const float sig = 1.0f / (1.0f + expf(-gl));
         o[i] = val * sig;
