@@ -5,11 +5,13 @@
 
 namespace mla {
 
-constexpr int VG_ROWS = 64;            // rows per workgroup
+constexpr int VG_ROWS = 64;            // rows per workgroup (fewer rows re-read W more often)
+constexpr int VG_RG = VG_ROWS / 16;    // 16-row groups (MFMA N tiles) per workgroup
+constexpr int VG_LD = VG_ROWS / 4;     // 16-B latent loads per thread
 constexpr int VG_PITCH = 512 + 8;      // LDS row pitch in bf16 (1040 B: conflict-free b128 reads)
 
-// Workgroup = (row block of 64, head, half of the 128 outputs).  Wave w
-// computes outputs v in [64*half + 16w, +16) for all 64 rows as
+// Workgroup = (row block of VG_ROWS, head, half of the 128 outputs).  Wave w
+// computes outputs v in [64*half + 16w, +16) for all rows of the block as
 // C[v][t] = W[h][v][:] . latent[t][h][:] on 16x16x32 bf16 MFMAs.  Each
 // lane prefetches its W fragments for all 16 K-steps up front (every W
 // element is read once); the latent block is staged once in LDS and read as
@@ -46,42 +48,42 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
     for (int s = 0; s < 16; ++s) a[s] = fp4x8_to_bf16x8(codes[s], e8m0_to_f32(sc4[s >> 2][s & 3]));
   }
 
-  // stage the latent block (64 rows x 64 chunks of 16 B) with all loads in
+  // stage the latent block (VG_ROWS rows x 64 chunks of 16 B) with all loads in
   // flight at once; the epilogue's gate values and row lengths are fetched
   // here too, so their latency hides behind the staging and the MFMAs
   {
-    u32x4 x[16];
+    u32x4 x[VG_LD];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < VG_LD; ++i) {
       const int c = tid + 256 * i, r = c >> 6, part = c & 63;
       x[i] = u32x4{0, 0, 0, 0};
       if (t0 + r < rows)
         x[i] = *reinterpret_cast<const u32x4*>(latent + (int64_t)(t0 + r) * l_row + h * l_head + part * 8);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < VG_LD; ++i) {
       const int c = tid + 256 * i, r = c >> 6, part = c & 63;
       *reinterpret_cast<u32x4*>(&lat[r * VG_PITCH + part * 8]) = x[i];
     }
   }
   const int col = h * MLA_D_V + 64 * blockIdx.z + 16 * wave + 4 * lg;
-  u32x2 gv[4];
-  int len[4];
+  u32x2 gv[VG_RG];
+  int len[VG_RG];
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {
+  for (int rg = 0; rg < VG_RG; ++rg) {
     const int t = min(t0 + 16 * rg + lr, rows - 1);  // rows past the end: a real row, not stored
     len[rg] = lengths[t / qlen];
     gv[rg] = *reinterpret_cast<const u32x2*>(gate + t * g_row + col);
   }
   __syncthreads();
 
-  f32x4 acc[4];
+  f32x4 acc[VG_RG];
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) acc[rg] = f32x4{0, 0, 0, 0};
+  for (int rg = 0; rg < VG_RG; ++rg) acc[rg] = f32x4{0, 0, 0, 0};
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
+    for (int rg = 0; rg < VG_RG; ++rg) {
       const bf16x8 b = *reinterpret_cast<const bf16x8*>(&lat[(16 * rg + lr) * VG_PITCH + 32 * s + 8 * lg]);
       acc[rg] = mfma16(a[s], b, acc[rg]);
     }
@@ -89,7 +91,7 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
 
   // epilogue: lane holds v = 64*half + 16w + 4lg + i for row t = t0 + 16rg + lr
 #pragma unroll
-  for (int rg = 0; rg < 4; ++rg) {
+  for (int rg = 0; rg < VG_RG; ++rg) {
     const int t = t0 + 16 * rg + lr;
     if (t >= rows) continue;
     u32x2 res = u32x2{0, 0};
