@@ -155,6 +155,27 @@ __device__ __forceinline__ float group_max4(float x) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// sum over the 4 lane groups {l, l^16, l^32, l^48}
+__device__ __forceinline__ float group_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// minimum over the 64 lanes, returned in a scalar register: rotations within
+// each 16-lane row (DPP), then the lane-group swaps
+__device__ __forceinline__ int wave_min64(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x124, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x122, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(x, x, 0x121, 0xF, 0xF, false));
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = min((int)a[0], (int)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return __builtin_amdgcn_readfirstlane(min((int)b[0], (int)b[1]));
+}
+
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -482,14 +503,24 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   __syncthreads();
   if (u >= nunits) return;
 
+  // this lane's rows (row group g, lane row lr) as (position in the qlen
+  // window, head); rows past M take the block's first row
+  int rj[NRG], rh[NRG];
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) {
+    const int m0 = m_lo + 16 * g + lr;
+    const int m = m0 < p.M ? m0 : m_lo;
+    rj[g] = m / p.heads;
+    rh[g] = m - p.heads * rj[g];
+  }
   auto fill_neginf = [&](int req, int k_from) {
     // LSE = -inf for splits [k_from, num_splits) of every row of this block
     const int nrows = min(RB, p.M - m_lo);
-    const int n = (p.num_splits - k_from) * nrows;
-    for (int i = tid; i < n; i += 256) {
-      const int k = k_from + i / nrows, m = m_lo + i % nrows;
+    if (tid < nrows) {
+      const int m = m_lo + tid;
       const int t = req * p.qlen + m / p.heads, h = m % p.heads;
-      p.lse[k * p.ls_s + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h] = -INFINITY;
+      float* dst = p.lse + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h;
+      for (int k = k_from; k < p.num_splits; ++k) dst[k * p.ls_s] = -INFINITY;
     }
   };
 
@@ -525,13 +556,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     for (int g = 0; g < NRG; ++g) {
       const int m = m_lo + 16 * g + lr;
       // rows past M compute on a copy of a real row; their results are discarded
-      const int vis = m < p.M ? L - p.qlen + m / p.heads + 1 : b;
+      const int vis = m < p.M ? L - p.qlen + rj[g] + 1 : b;
       lim[g] = min(b, vis);
       lim_min = min(lim_min, lim[g]);
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, s));
-    lim_min = __builtin_amdgcn_readfirstlane(lim_min);  // wave-uniform: keep the mask test scalar
+    lim_min = wave_min64(lim_min);  // wave-uniform: keep the mask test scalar
 
     // ---- stage the block's query rows and the first segment's cache
     // indices in LDS with direct global->LDS loads (one round trip)
@@ -712,9 +741,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     // ---------------------------------------------------- piece epilogue
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
-      float l = lsum[g];
-      l += __shfl_xor(l, 16);
-      l += __shfl_xor(l, 32);
+      const float l = group_sum4(lsum[g]);
       if (lg == 0) redsum[(16 * g + lr) * 4 + wave] = l;
     }
     __syncthreads();
@@ -724,11 +751,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       const float l = ((s4[0] + s4[1]) + s4[2]) + s4[3];
       const int m = m_lo + 16 * g + lr;
       if (m >= p.M) continue;
-      const int t = r * p.qlen + m / p.heads, h = m % p.heads;
+      const int t = r * p.qlen + rj[g], h = rh[g];
       // l == 0: no visible token in this split.  A NaN l (NaN cache bytes or
       // an invalid index) is written through, so it poisons the row.
       if (l != 0.0f) {
-        const float inv = p.kv_scale / l;
+        const float inv = p.kv_scale * __builtin_amdgcn_rcpf(l);
         uint16_t* orow =
             p.o + k * p.os_s + (int64_t)t * p.os_r + (int64_t)h * p.os_h + 128 * wave + 4 * lg;
 #pragma unroll
