@@ -126,8 +126,9 @@ int mla_split_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_spl
                    int64_t* chunk_out);
 
 /*
- * LSE merge of the split partials ([MLA] `m1c_inputs`: "M1b merges the
- * splits"; the same combine `post` applies across ranks).  For row t, head h:
+ * LSE merge of the split partials ([MLA] `m1c_inputs`: the step after the
+ * partials combines the splits; `post` applies the same combine across
+ * ranks).  For row t, head h:
  *   m = max_k lse_k;  m = -inf  ->  o = 0, lse = -inf;  otherwise
  *   lse = m + ln sum_k exp(lse_k - m),   o = bf16( sum_k exp(lse_k - lse) * o_k )
  * Splits with lse_k = -inf are skipped and their o_k is never read.

@@ -109,6 +109,11 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* gsrc, uint32_t lds_base
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(gsrc)
                : "memory", "m0");
 }
+// 4-byte variant: lane l writes lds_base + 4l
+__device__ __forceinline__ void lds_dma4(const int32_t* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(gsrc)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -180,19 +185,18 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Direct global->LDS staging of up to IDX_CAP cache indices (16 B = 4
-// indices per lane per load; chunks past n load chunk 0 again).
+// Direct global->LDS staging of n (1 <= n <= IDX_CAP) cache indices, one
+// per lane per load; entries past n repeat entry n-1, so nothing past the
+// source range is read.
 __device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int32_t* idx_lds, int wave, int lane) {
-  const int nch = (n + 3) >> 2;
   // rolled on purpose: the per-lane addresses are recomputed in place
   // rather than hoisted (and spilled) across the piece loop
 #pragma unroll 1
-  for (int j = 0; j < IDX_CAP / 1024; ++j) {
-    const int blk = wave + 4 * j;  // 1 KB = 256 indices per load instruction
-    const int ch = 64 * blk + lane;
-    const int32_t* g = src + 4 * (ch < nch ? ch : 0);
-    const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(idx_lds + 256 * blk));
-    if (64 * blk < nch) lds_dma16(reinterpret_cast<const uint8_t*>(g), d);
+  for (int j = 0; j < IDX_CAP / 256; ++j) {
+    const int blk = wave + 4 * j;  // 64 indices per load instruction
+    const int i = 64 * blk + lane;
+    const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(idx_lds + 64 * blk));
+    if (64 * blk < n) lds_dma4(src + (i < n ? i : n - 1), d);
   }
 }
 
@@ -419,6 +423,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
   __shared__ __attribute__((aligned(16))) uint8_t qlds_[QL_BYTES];
   __shared__ int32_t red_i[4];
+  __shared__ int64_t rowoff[RB];  // output offset of block row i within its request, -1 past M
+  // the normalised O rows are staged as bf16 [RB][O_PITCH] in the tile buffers
+  constexpr int O_PITCH = MLA_D_LATENT + 16;  // +32 B: rows start 8 banks apart
+  static_assert(RB * O_PITCH * 2 <= NBUF * TILE_BYTES, "O staging fits the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -500,6 +508,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   __shared__ int32_t rP[RMAX + 1];
   const int nreq = min(r_end - r, RMAX);
   for (int i = tid; i <= nreq; i += 256) rP[i] = ip(r + i) - base;
+  if (tid < RB) {
+    const int m = m_lo + tid;
+    rowoff[tid] = m < p.M ? (int64_t)(m / p.heads) * p.os_r + (int64_t)(m % p.heads) * p.os_h : -1;
+  }
   __syncthreads();
   if (u >= nunits) return;
 
@@ -739,35 +751,58 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }  // while (again)
 
     // ---------------------------------------------------- piece epilogue
+    // The row sums; O normalised to bf16 into LDS (every wave is past its
+    // last PV after the first barrier, so the tile buffers are free), then
+    // written out one whole 1 KB row per store instruction.
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
       const float l = group_sum4(lsum[g]);
       if (lg == 0) redsum[(16 * g + lr) * 4 + wave] = l;
     }
     __syncthreads();
+    MLA_LDS uint16_t* ost = (MLA_LDS uint16_t*)kbuf;
+    uint64_t wmask = 0;  // block rows to write (a finite or NaN sum, row < M)
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
       const f32x4 s4 = *reinterpret_cast<const f32x4*>(&redsum[(16 * g + lr) * 4]);
       const float l = ((s4[0] + s4[1]) + s4[2]) + s4[3];
-      const int m = m_lo + 16 * g + lr;
-      if (m >= p.M) continue;
-      const int t = r * p.qlen + rj[g], h = rh[g];
-      // l == 0: no visible token in this split.  A NaN l (NaN cache bytes or
-      // an invalid index) is written through, so it poisons the row.
-      if (l != 0.0f) {
-        const float inv = p.kv_scale * __builtin_amdgcn_rcpf(l);
-        uint16_t* orow =
-            p.o + k * p.os_s + (int64_t)t * p.os_r + (int64_t)h * p.os_h + 128 * wave + 4 * lg;
+      // l == 0: no visible token in this split (the row is not written).  A
+      // NaN l (NaN cache bytes or an invalid index) is written through, so
+      // it poisons the row.
+      const float inv = p.kv_scale * __builtin_amdgcn_rcpf(l);
+      MLA_LDS uint16_t* orow = ost + (16 * g + lr) * O_PITCH + 128 * wave + 4 * lg;
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          const f32x4 v = O[d][g];
-          *reinterpret_cast<u32x2*>(orow + 16 * d) =
-              u32x2{pk_bf16(v[0] * inv, v[1] * inv), pk_bf16(v[2] * inv, v[3] * inv)};
-        }
+      for (int d = 0; d < 8; ++d) {
+        const f32x4 v = O[d][g];
+        *reinterpret_cast<MLA_LDS u32x2*>(orow + 16 * d) =
+            u32x2{pk_bf16(v[0] * inv, v[1] * inv), pk_bf16(v[2] * inv, v[3] * inv)};
       }
-      if (wave == 0 && lg == 0)
+      const int m = m_lo + 16 * g + lr;
+      wmask |= (__ballot(l != 0.0f && m < p.M) & 0xFFFFull) << (16 * g);  // lanes lg == 0: rows 16g + lr
+      if (wave == 0 && lg == 0 && m < p.M) {
+        const int t = r * p.qlen + rj[g], h = rh[g];
         p.lse[k * p.ls_s + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h] =
             l != 0.0f ? (mref[g] + __log2f(l)) * kLn2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    {
+      // this wave's rows wave, wave+4, ...: all LDS reads first, then the stores
+      uint16_t* obase = p.o + k * p.os_s + (int64_t)r * p.qlen * p.os_r + 8 * lane;
+      const int wu = __builtin_amdgcn_readfirstlane(wave);
+      u32x4 ov[RB / 4];
+      int64_t off[RB / 4];
+#pragma unroll
+      for (int j = 0; j < RB / 4; ++j) {
+        ov[j] = *reinterpret_cast<const MLA_LDS u32x4*>(ost + (wu + 4 * j) * O_PITCH + 8 * lane);
+        off[j] = rowoff[wu + 4 * j];
+      }
+      // keep the reads together, ahead of the (conditional) stores
+#pragma unroll
+      for (int j = 0; j < RB / 4; ++j) asm volatile("" : "+v"(ov[j]), "+v"(off[j]));
+#pragma unroll
+      for (int j = 0; j < RB / 4; ++j)
+        if ((wmask >> (wu + 4 * j)) & 1) *reinterpret_cast<u32x4*>(obase + off[j]) = ov[j];
     }
     __syncthreads();
   }

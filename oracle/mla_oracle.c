@@ -131,7 +131,7 @@ double orc_e8m0_decode(uint8_t b) {
  * token i's row is [kv_c (512) | k_pe (64)], each value divided by kv_scale
  * in binary32 and encoded with E, stored at row slot_mapping[i].  A negative
  * slot skips the token.  Reading taken: the division is a correctly rounded
- * binary32 division, as written "x / k_scale". */
+ * binary32 division of each value by the scale. */
 void orc_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                   int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n,
                   uint8_t* kv_cache, float kv_scale) {
@@ -275,8 +275,9 @@ void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t 
 
 /* -------------------------------------------------------------- merge */
 
-/* LSE merge of split partials ([MLA] `m1c_inputs`: "M1b merges the splits";
- * the same combine `post` applies across ranks).  For each (row, head):
+/* LSE merge of split partials ([MLA] `m1c_inputs`: the step after the
+ * partials combines the splits; `post` applies the same combine across
+ * ranks).  For each (row, head):
  *   m = max_k LSE_k; if m = -inf: o = 0, LSE = -inf; otherwise
  *   LSE = m + ln sum_k exp(LSE_k - m),  o = sum_k exp(LSE_k - LSE) * o_k
  * where o_k is the stored bf16 partial.  Splits with LSE_k = -inf contribute
