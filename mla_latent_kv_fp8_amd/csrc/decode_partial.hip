@@ -206,15 +206,23 @@ __device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int
 // and dims [64 QR, 576) to the piece-resident area qlds + i*qpitch_lds.  A
 // row takes 8 chunks of 16 B per 64 dims plus one chunk of padding (which
 // staggers the rows over the LDS banks).
-template <int NRG> constexpr int qpitch_reg() { return 16 * (8 * qreg_pairs<NRG>() + 1); }
+// chunks per staged row of the register part: 8 per K-step pair, plus one of
+// padding where the block still fits the one tile buffer it is staged in
+template <int NRG> constexpr int qw_reg() {
+  return 16 * NRG * (8 * qreg_pairs<NRG>() + 1) <= TILE_BYTES / 16 ? 8 * qreg_pairs<NRG>() + 1 : 8 * qreg_pairs<NRG>();
+}
+template <int NRG> constexpr int qpitch_reg() { return 16 * qw_reg<NRG>(); }
 template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 1); }
 
 template <int NRG>
-__device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
-                                                int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
-                                                MLA_LDS int32_t* idx_lds, int wave, int lane) {
+__device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
+                                               int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
+                                               MLA_LDS int32_t* idx_lds, int wave, int lane) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
+  // the indices go first: the caller waits for them alone and issues the
+  // first tiles while the query is still in flight
+  stage_idx(idx_src, nidx, idx_lds, wave, lane);
   const uint16_t* q_base = p.q + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
   auto src_of = [&](int row, int dim8) -> const uint16_t* {
     const int m = m_lo + row;
@@ -222,17 +230,20 @@ __device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int
     const int jj = m / p.heads, h = m - p.heads * jj;
     return p.q + (int64_t)(r * p.qlen + jj) * p.q_sr + (int64_t)h * p.q_sh + dim8;
   };
+  int nq = 0;
   // part 0: register dims
   {
-    constexpr int W = 8 * QR + 1;
+    constexpr int W = qw_reg<NRG>();
     constexpr int NR = (RB * W + 63) / 64;
+    static_assert(NR * 1024 <= TILE_BYTES, "the register part is staged in one tile buffer");
+    nq += (NR - wave + 3) / 4;
 #pragma unroll 1
     for (int j0 = 0; j0 < NR; j0 += 4) {
       const int j = j0 + wave;
       if (j < NR) {
         const int c = 64 * j + lane;
         const int row = c / W, part = c - W * (c / W);
-        const uint16_t* g = part < W - 1 ? src_of(row, 8 * part) : q_base;
+        const uint16_t* g = part < 8 * QR ? src_of(row, 8 * part) : q_base;
         lds_dma16(reinterpret_cast<const uint8_t*>(g),
                   __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qreg + 1024 * j)));
       }
@@ -241,6 +252,7 @@ __device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int
   if constexpr (QR < 9) {
     constexpr int W = 8 * (9 - QR) + 1;
     constexpr int NL = (RB * W + 63) / 64;
+    nq += (NL - wave + 3) / 4;
 #pragma unroll 1
     for (int j0 = 0; j0 < NL; j0 += 4) {
       const int j = j0 + wave;
@@ -253,7 +265,36 @@ __device__ __forceinline__ void stage_q_and_idx(const PartialArgs& p, int r, int
       }
     }
   }
-  stage_idx(idx_src, nidx, idx_lds, wave, lane);
+  return nq;
+}
+
+// A valid cache row among the first n staged indices (0 if there is none),
+// loaded in place of padding and invalid entries.
+__device__ __forceinline__ int first_valid_row(const int32_t* idx, int n, int64_t num_slots) {
+  int v = idx[0];
+  if ((uint32_t)v >= (uint64_t)num_slots) {
+    v = 0;
+    for (int i = 1; i < n; ++i)
+      if ((uint32_t)idx[i] < (uint64_t)num_slots) { v = idx[i]; break; }
+  }
+  return v;
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n: at most n of this wave's loads
+// may still be in flight (loads complete in issue order)
+__device__ __forceinline__ void wait_vm_upto(int n) {
+  switch (n) {
+#define MLA_WAIT_CASE(k) \
+  case k:                \
+    asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); \
+    break;
+    MLA_WAIT_CASE(0) MLA_WAIT_CASE(1) MLA_WAIT_CASE(2) MLA_WAIT_CASE(3) MLA_WAIT_CASE(4) MLA_WAIT_CASE(5)
+    MLA_WAIT_CASE(6) MLA_WAIT_CASE(7) MLA_WAIT_CASE(8) MLA_WAIT_CASE(9) MLA_WAIT_CASE(10) MLA_WAIT_CASE(11)
+    MLA_WAIT_CASE(12) MLA_WAIT_CASE(13) MLA_WAIT_CASE(14) MLA_WAIT_CASE(15) MLA_WAIT_CASE(16)
+#undef MLA_WAIT_CASE
+    default:
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // more than 16: wait for everything
+  }
 }
 
 // Scheduling hint for one unrolled step: NM groups of (1 MFMA, a share of NV
@@ -411,8 +452,6 @@ template <int NRG>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
-  static_assert(((RB * (8 * QR + 1) + 63) / 64) * 1024 <= (NBUF - 1) * TILE_BYTES,
-                "query staging must fit in two tile buffers");
   constexpr int QL_BYTES = QR < 9 ? ((RB * (8 * (9 - QR) + 1) + 63) / 64) * 1024 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
@@ -574,12 +613,30 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
     lim_min = wave_min64(lim_min);  // wave-uniform: keep the mask test scalar
 
-    // ---- stage the block's query rows and the first segment's cache
-    // indices in LDS with direct global->LDS loads (one round trip)
-    MLA_LDS uint8_t* qst = kbuf + TILE_BYTES;
-    stage_q_and_idx<NRG>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
-    wait_vm_all();
+    // ---- stage the first segment's cache indices and the block's query
+    // rows in LDS with direct global->LDS loads; the register part of the
+    // query goes to tile buffer 2 (tile 2 is issued only after every wave
+    // has read it).  Only the indices are waited for here: tiles 0 and 1
+    // are issued while the query is still in flight.
+    MLA_LDS uint8_t* qst = kbuf + 2 * TILE_BYTES;
+    const int nq = stage_q_and_idx<NRG>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
+    wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
+    {
+      const int slen = min(IDX_CAP, b - a);
+      const int safe_row = first_valid_row(idx, slen, p.num_slots);
+      issue_tile(p.kv, p.num_slots, tile_row(idxl, min(NT, slen), wave, lane), safe_row, kbuf, wave, lane);
+      if (slen > NT)
+        issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
+                   kbuf + TILE_BYTES, wave, lane);
+      // the query (issued before the tiles) and tile 0 have landed; tile 1's
+      // 9 loads may still fly
+      if (slen > NT)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        wait_vm_all();
+      __syncthreads();
+    }
     // query fragments for K-step pairs pp < QR: K-step 2pp uses dims
     // 64pp+16lg..+7, 2pp+1 the next 8 (the K fragments use the same order)
     bf16x8 qf[NRG][2 * QR];
@@ -598,6 +655,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     for (int g = 0; g < NRG; ++g)
 #pragma unroll
       for (int ss = 0; ss < 2 * (NRG >= 3 && QPIN3 < QR ? QPIN3 : QR); ++ss) asm volatile("" : "+a"(qf[g][ss]));
+
 
     f32x4 O[8][NRG];
     // per row: reference (log2 units), raw-score threshold of the flag, -ref
@@ -627,34 +685,27 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
 
     for (int s0 = a; s0 < b && !again; s0 += IDX_CAP) {
       const int slen = min(IDX_CAP, b - s0);
-      if (s0 != a || restaged) {
+      const bool first_seg = s0 == a && !restaged;  // staged and issued with the query
+      if (!first_seg) {
         // ---- a later segment (or a restart): stage its cache indices
         __syncthreads();  // the previous segment's tiles are done with idx / kbuf
         stage_idx(rows_r + s0, slen, idxl, wave, lane);
         wait_vm_all();
         __syncthreads();
       }
-      int safe_row = 0;  // a valid row of this segment, for padding loads
-      {
-        int v = idx[0];
-        if ((uint32_t)v >= (uint64_t)p.num_slots) {
-          v = 0;
-          for (int i = 1; i < slen; ++i)
-            if ((uint32_t)idx[i] < (uint64_t)p.num_slots) { v = idx[i]; break; }
-        }
-        safe_row = v;
-      }
+      const int safe_row = first_valid_row(idx, slen, p.num_slots);
       const int ntiles = (slen + NT - 1) / NT;
-      issue_tile(p.kv, p.num_slots, tile_row(idxl, min(NT, slen), wave, lane), safe_row, kbuf, wave, lane);
-      __syncthreads();  // every wave has its query fragments: buffer 1 is free
-      if (ntiles > 1)
-        issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
-                   kbuf + TILE_BYTES, wave, lane);
-      if (ntiles > 1)
-        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0's 9 loads (tile 1's may fly)
-      else
-        wait_vm_all();
-      __syncthreads();
+      if (!first_seg) {
+        issue_tile(p.kv, p.num_slots, tile_row(idxl, min(NT, slen), wave, lane), safe_row, kbuf, wave, lane);
+        if (ntiles > 1)
+          issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
+                     kbuf + TILE_BYTES, wave, lane);
+        if (ntiles > 1)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0's 9 loads (tile 1's may fly)
+        else
+          wait_vm_all();
+        __syncthreads();
+      }
 
       // One barrier per tile.  Each wave computes its quarter's scores and
       // P against the shared reference optimistically and flags the rows
