@@ -1,7 +1,7 @@
 // W_UV value projection fused with the FP32 sigmoid gate (the value step of
 // the decode runtime's `post`; MlaValue / MlaGate semantics: bf16 value times
 // the FP32 sigmoid, rounded to bf16; rows of empty requests are +0).
-#include "common.hpp"
+#include "post_common.hpp"
 
 namespace mla {
 
@@ -31,22 +31,7 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
 
   // W fragments of all 16 K-steps (lane: output v, latents 32s + 8lg .. +7)
   bf16x8 a[16];
-  if (FMT == MLA_W_BF16) {
-    const uint16_t* wp = reinterpret_cast<const uint16_t*>(w_uv) + h * w_head + v * w_v + 8 * lg;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) a[s] = *reinterpret_cast<const bf16x8*>(wp + 32 * s);
-  } else {
-    const uint8_t* wp = reinterpret_cast<const uint8_t*>(w_uv) + h * w_head + v * w_v + 4 * lg;
-    const uint8_t* sp = w_scale + h * ws_head + v * ws_v;
-    uint32_t codes[16];
-    u32x4 sc4[4];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) codes[s] = *reinterpret_cast<const uint32_t*>(wp + 16 * s);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sc4[i] = u32x4{sp[4 * i], sp[4 * i + 1], sp[4 * i + 2], sp[4 * i + 3]};
-#pragma unroll
-    for (int s = 0; s < 16; ++s) a[s] = fp4x8_to_bf16x8(codes[s], e8m0_to_f32(sc4[s >> 2][s & 3]));
-  }
+  load_w_frags<FMT>(w_uv, w_head, w_v, w_scale, ws_head, ws_v, h, v, lg, a);
 
   // stage the latent block (VG_ROWS rows x 64 chunks of 16 B) with all loads in
   // flight at once; the epilogue's gate values and row lengths are fetched
@@ -94,20 +79,7 @@ __global__ void __launch_bounds__(256) value_gate_kernel(
   for (int rg = 0; rg < VG_RG; ++rg) {
     const int t = t0 + 16 * rg + lr;
     if (t >= rows) continue;
-    u32x2 res = u32x2{0, 0};
-    if (len[rg] > 0) {
-      float o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float val = bf16_bits_to_f32(f32_to_bf16_bits(acc[rg][i]));
-        const uint32_t gb = (i & 1) ? (gv[rg][i >> 1] >> 16) : (gv[rg][i >> 1] & 0xFFFFu);
-        const float gl = bf16_bits_to_f32(gb);
-        const float sig = 1.0f / (1.0f + expf(-gl));
-        o[i] = val * sig;
-      }
-      res = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
-    *reinterpret_cast<u32x2*>(out + t * out_row + col) = res;
+    *reinterpret_cast<u32x2*>(out + t * out_row + col) = gate_out(acc[rg], gv[rg], len[rg]);
   }
 }
 
