@@ -60,11 +60,13 @@ struct PartialArgs {
 
 // LDS layout of a staged tile (64 tokens x 36 chunks of 16 B): block
 // (t/16, c/4) of 1 KB holds 16 tokens x 4 chunks; inside it, chunk c of
-// token t sits at 16-B slot 4*(t%16) + ((c%4) ^ h(t)).  With 32 banks the
-// QK fragment read (8 consecutive tokens, one chunk) and the transposed V
-// read (tokens {4G..4G+3} and {16+4G..16+4G+3}, one chunk) both hit 8
-// distinct 16-byte bank groups.
-__device__ __forceinline__ int hsw(int t) { return ((t >> 1) & 3) ^ (((t >> 4) & 1) << 1); }
+// token t sits at 16-B slot 4*(t%16) + ((c%4) ^ h(t)).  This h makes both
+// the QK fragment reads (16 tokens of a quarter, one chunk each) and the
+// transposed V reads (tokens {4G..4G+3} and {16+4G..16+4G+3}, 8-byte
+// halves) free of bank conflicts on gfx950 (measured with the LDS
+// bank-conflict counter: flipping only bit 1 for the second 16 tokens
+// left the V reads 2-way conflicted).
+__device__ __forceinline__ int hsw(int t) { return ((t >> 1) & 3) ^ (((t >> 4) & 1) * 3); }
 __device__ __forceinline__ int tile_off(int t, int c) {
   return 16 * (64 * (9 * (t >> 4) + (c >> 2)) + 4 * (t & 15) + ((c & 3) ^ hsw(t)));
 }
@@ -203,16 +205,19 @@ __device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int
 // Query rows of one block plus the first index segment, all by direct
 // global->LDS loads.  With QR = qreg_pairs<NRG>(), dims [0, 64 QR) of row i
 // go to the staging area at qreg + i*qpitch_reg (read once into registers)
-// and dims [64 QR, 576) to the piece-resident area qlds + i*qpitch_lds.  A
-// row takes 8 chunks of 16 B per 64 dims plus one chunk of padding (which
-// staggers the rows over the LDS banks).
-// chunks per staged row of the register part: 8 per K-step pair, plus one of
-// padding where the block still fits the one tile buffer it is staged in
+// and dims [64 QR, 576) to the piece-resident area qlds + i*qpitch_lds
+// (layout below).  The register part takes 8 chunks of 16 B per 64 dims
+// plus one chunk of padding (which staggers the rows over the LDS banks)
+// where the block still fits the one tile buffer it is staged in.
 template <int NRG> constexpr int qw_reg() {
   return 16 * NRG * (8 * qreg_pairs<NRG>() + 1) <= TILE_BYTES / 16 ? 8 * qreg_pairs<NRG>() + 1 : 8 * qreg_pairs<NRG>();
 }
 template <int NRG> constexpr int qpitch_reg() { return 16 * qw_reg<NRG>(); }
-template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 1); }
+// The LDS part holds, per row, 8 chunks per K-step pair in the order the
+// QK reads them (chunk 4h + lg of a pair: dims 16lg + 8h .. +7 of it, so
+// one read instruction covers 64 contiguous bytes of each row), plus two
+// chunks of padding: a 544-byte pitch (48 rows) has no bank conflicts.
+template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 2); }
 
 template <int NRG>
 __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
@@ -250,7 +255,7 @@ __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int 
     }
   }
   if constexpr (QR < 9) {
-    constexpr int W = 8 * (9 - QR) + 1;
+    constexpr int W = qpitch_lds<NRG>() / 16;
     constexpr int NL = (RB * W + 63) / 64;
     nq += (NL - wave + 3) / 4;
 #pragma unroll 1
@@ -259,7 +264,9 @@ __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int 
       if (j < NL) {
         const int c = 64 * j + lane;
         const int row = c / W, part = c - W * (c / W);
-        const uint16_t* g = part < W - 1 ? src_of(row, 64 * QR + 8 * part) : q_base;
+        // chunk part = 8p + 4h + lg of the row: dims 64(QR + p) + 16lg + 8h
+        const int dim = 64 * (QR + (part >> 3)) + 16 * (part & 3) + 8 * ((part >> 2) & 1);
+        const uint16_t* g = part < 8 * (9 - QR) ? src_of(row, dim) : q_base;
         lds_dma16(reinterpret_cast<const uint8_t*>(g),
                   __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qlds + 1024 * j)));
       }
@@ -386,7 +393,7 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
 #pragma unroll
   for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
   const MLA_LDS uint8_t* kq = kt + tile_off(16 * wave + lr, lg);
-  const MLA_LDS uint8_t* qq = qlds + lr * qpitch_lds<NRG>() + 32 * lg - 128 * QR;
+  const MLA_LDS uint8_t* qq = qlds + lr * qpitch_lds<NRG>() + 16 * lg - 128 * QR;
   u32x4 raw[3];
   raw[0] = *(const MLA_LDS u32x4*)kq;
   raw[1] = *(const MLA_LDS u32x4*)(kq + 1024);
@@ -395,7 +402,7 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
 #pragma unroll
     for (int g = 0; g < NRG; ++g)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ql[0][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 16 * h);
+      for (int h = 0; h < 2; ++h) ql[0][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 64 * h);
   }
   bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
   bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
@@ -407,7 +414,7 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
       for (int g = 0; g < NRG; ++g)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          ql[(pp + 1) & 1][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + 1) + 16 * h);
+          ql[(pp + 1) & 1][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + 1) + 64 * h);
     }
     bf16x8 nlo = klo, nhi = khi;
     if (pp + 1 < 9) {
@@ -452,7 +459,7 @@ template <int NRG>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
-  constexpr int QL_BYTES = QR < 9 ? ((RB * (8 * (9 - QR) + 1) + 63) / 64) * 1024 : 16;
+  constexpr int QL_BYTES = QR < 9 ? ((RB * (qpitch_lds<NRG>() / 16) + 63) / 64) * 1024 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
