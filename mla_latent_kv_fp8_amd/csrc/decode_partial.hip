@@ -755,7 +755,9 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
 #pragma unroll
         for (int g = 0; g < NRG; ++g)
           need |= fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3])) > thr[g];
-        if (lane == 0) redflag[4 * (it & 1) + wave] = __any(need) ? 1 : 0;
+        // (the vote runs on all lanes, outside the single-lane store)
+        const bool any_need = __any(need);
+        if (lane == 0) redflag[4 * (it & 1) + wave] = any_need ? 1 : 0;
         float ps[NRG];
         p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
         i32x2 v0[8];

@@ -15,6 +15,16 @@ pytestmark = pytest.mark.gpu
 O_TOL, LSE_TOL, OUT_REL_TOL = 1e-2, 1e-3, 2e-2
 
 
+def o_err_ok(got, ref):
+    """|got - ref| <= max(1e-2, 2^-7 |ref|), elementwise.  o is bf16 (and so
+    is P inside the kernel), so beyond |ref| ~ 1.3 a correct result can
+    differ from the rounded exact value by one bf16 ulp at its magnitude;
+    below that the bound is the plain 1e-2."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return bool(np.all(np.abs(got - ref) <= np.maximum(O_TOL, np.abs(ref) * 2.0 ** -7)))
+
+
 def lse_err_ok(got, ref):
     """|got - ref| <= 1e-3 plus 8 f32 ulps of |ref|: the LSE output is f32, so
     for very large scores (|LSE| ~ 1e4) its own resolution exceeds 1e-3."""
@@ -123,8 +133,7 @@ def _check_partials(oracle, w, st, cache):
     assert np.array_equal(np.isneginf(lse), ~fin), "empty-split pattern differs"
     assert lse_err_ok(lse[fin], l_ref[fin])
     o_ref_b = oracle.bf16_decode(oracle.bf16_round(o_ref))
-    err = np.abs(o[fin] - o_ref_b[fin]).max(initial=0)
-    assert err <= O_TOL, err
+    assert o_err_ok(o[fin], o_ref_b[fin]), np.abs(o[fin] - o_ref_b[fin]).max(initial=0)
     return bounds
 
 
@@ -137,7 +146,7 @@ def _check_merge_and_value(oracle, w, st):
     lat = _np_bf16(st.latent)
     got = oracle.bf16_decode(lat[:, :H])
     want = oracle.bf16_decode(oracle.bf16_round(mo))
-    assert np.abs(got - want).max(initial=0) <= O_TOL
+    assert o_err_ok(got, want), np.abs(got - want).max(initial=0)
     gl = st.lse.cpu().numpy()
     assert np.array_equal(np.isneginf(gl), np.isneginf(ml))
     fin = np.isfinite(ml)
@@ -368,7 +377,7 @@ def test_single_split_and_one_token(ops, oracle):
     # L = 1: o equals kv_scale times the (only) value row
     row = oracle.fp8_decode(cache[w.indices[0]])[:512] * w.kv_scale
     got = oracle.bf16_decode(_np_bf16(st.latent)[0, 0])
-    assert np.abs(got - row).max() <= O_TOL
+    assert o_err_ok(got, row)
 
 
 # ------------------------------------------- full size, sampled (bench launch)
@@ -411,13 +420,13 @@ def test_full_size_sampled(ops, oracle, name):
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isneginf(lse), ~fin)
     assert np.abs(lse[fin] - l_ref[fin]).max(initial=0) <= LSE_TOL
-    assert np.abs(o[fin] - oracle.bf16_decode(oracle.bf16_round(o_ref))[fin]).max(initial=0) <= O_TOL
+    assert o_err_ok(o[fin], oracle.bf16_decode(oracle.bf16_round(o_ref))[fin])
     # merged latent of the sampled rows against the oracle's unsplit attention
     one = np.stack([np.zeros(len(sample), np.int32), sub_ptr[1:] - sub_ptr[:-1]], 1).astype(np.int32)
     o1, l1 = oracle.decode_partial(q, cache, sub_ptr, sub_idx, one, w.qlen, w.sm_scale, w.kv_scale)
     lat = oracle.bf16_decode(_np_bf16(st.latent[torch.from_numpy(rows_t).cuda(), :H]))
     f1 = np.isfinite(l1[0])
-    assert np.abs(lat[f1] - o1[0][f1]).max(initial=0) <= O_TOL
+    assert o_err_ok(lat[f1], o1[0][f1])
     assert (lat[~f1] == 0).all()
     # gated output rows: oracle value+gate on the GPU latent rows
     latb = _np_bf16(st.latent[torch.from_numpy(rows_t).cuda()])
@@ -441,6 +450,30 @@ def test_rebase_on_late_spike(ops, oracle):
     for r, tok in ((0, 30), (1, 50)):
         row = w.indptr[r] + tok
         sign = np.where(qd[r, r % w.heads] >= 0, 1.0, -1.0).astype(np.float32)
+        w.kv_rows[row] = synth.to_bf16_bits(448.0 * sign)
+    w.slot_mapping[:] = -1  # keep the spike rows (no new-token overwrite)
+    st = DeviceStep(w, num_workers=2, split_min_tokens=1)
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
+
+
+def test_restart_in_a_later_segment(ops, oracle):
+    """A score spike in the third index segment of a 5000-token piece: the
+    piece restarts from its first segment (the indices are staged again)
+    with the new reference.  Exact attention still holds."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("restart from a later segment (5000-token pieces)")
+    w = synth.make("batch", batch=2, len_range=(5000, 5000))
+    qd = oracle.bf16_decode(w.q)
+    for r, tok in ((0, 4500), (1, 2100)):
+        row = w.indptr[r] + tok
+        h = 7 + r
+        sign = np.where(qd[r, h] >= 0, 1.0, -1.0).astype(np.float32)
         w.kv_rows[row] = synth.to_bf16_bits(448.0 * sign)
     w.slot_mapping[:] = -1  # keep the spike rows (no new-token overwrite)
     st = DeviceStep(w, num_workers=2, split_min_tokens=1)
