@@ -460,14 +460,18 @@ def test_rebase_on_late_spike(ops, oracle):
     _check_merge_and_value(oracle, w, st)
 
 
-def test_restart_in_a_later_segment(ops, oracle):
+@pytest.mark.parametrize("heads", [16, 32, 96])
+def test_restart_in_a_later_segment(ops, oracle, heads, monkeypatch):
     """A score spike in the third index segment of a 5000-token piece: the
     piece restarts from its first segment (the indices are staged again)
-    with the new reference.  Exact attention still holds."""
+    with the new reference.  Exact attention still holds.  16, 32 and 96
+    heads run the 16-, 32- and 48-row workgroup variants."""
     from mla_latent_kv_fp8_amd import synth
     from mla_latent_kv_fp8_amd.step import DeviceStep
 
-    _announce("restart from a later segment (5000-token pieces)")
+    _announce(f"restart from a later segment (5000-token pieces, {heads} heads)")
+    spec = dict(synth.SPECS["batch"], heads=heads, heads_pad=128 if heads == 96 else heads)
+    monkeypatch.setitem(synth.SPECS, "batch", spec)
     w = synth.make("batch", batch=2, len_range=(5000, 5000))
     qd = oracle.bf16_decode(w.q)
     for r, tok in ((0, 4500), (1, 2100)):
@@ -481,4 +485,19 @@ def test_restart_in_a_later_segment(ops, oracle):
     torch.cuda.synchronize()
     cache = _oracle_cache(oracle, w)
     _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
+
+
+def test_unit_with_many_requests(ops, oracle):
+    """Units that cover more than 64 requests (short requests, two workers):
+    the request offsets past the first 64 of a unit are read from global
+    memory instead of the LDS cache."""
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce("units of more than 64 requests")
+    w = synth.make("batch", batch=180, len_range=(1, 24))
+    st = _run_step(ops, w, num_workers=2, split_min_tokens=1)
+    cache = _oracle_cache(oracle, w)
+    assert np.array_equal(st.kv_cache.cpu().numpy(), cache)
+    bounds = _check_partials(oracle, w, st, cache)
     _check_merge_and_value(oracle, w, st)
