@@ -501,3 +501,28 @@ def test_unit_with_many_requests(ops, oracle):
     assert np.array_equal(st.kv_cache.cpu().numpy(), cache)
     bounds = _check_partials(oracle, w, st, cache)
     _check_merge_and_value(oracle, w, st)
+
+
+def test_restart_inside_the_speculative_window(ops, oracle):
+    """qlen = 4: a spike on the second-to-last token of each request, which
+    only the window's last two rows see.  Those rows restart the piece with
+    a new reference; the earlier rows keep the token masked."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("restart inside the speculative window (qlen 4)")
+    w = synth.make("spec_q4", batch=2, len_range=(3000, 3000))
+    qd = oracle.bf16_decode(w.q)
+    for r in range(2):
+        row = w.indptr[r + 1] - 2
+        t = r * w.qlen + w.qlen - 1  # the window's last row sees it
+        h = 11 + r
+        sign = np.where(qd[t, h] >= 0, 1.0, -1.0).astype(np.float32)
+        w.kv_rows[row] = synth.to_bf16_bits(448.0 * sign)
+    w.slot_mapping[:] = -1  # keep the spike rows (no new-token overwrite)
+    st = DeviceStep(w, num_workers=2, split_min_tokens=1)
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
