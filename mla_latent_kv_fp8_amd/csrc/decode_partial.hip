@@ -11,35 +11,38 @@
 //    feeds every head: QK and PV are dense MFMA contractions.
 //  * Per 64-token tile: the gathered fp8 rows (576 B each) are staged once in
 //    LDS in swizzled 1 KB blocks of 16 tokens x 64 bytes, by asynchronous
-//    global->LDS loads into a double buffer (tile i+1 streams in while tile
-//    i is computed); the cache indices of a piece are staged in LDS first
-//    (2048 at a time), with the query rows, by the same direct loads.
+//    global->LDS loads, triple buffered (the loads of tile i+2 are issued
+//    while tile i is computed).  A piece's cache indices (2048 at a time)
+//    and its query rows are staged by the same direct loads; the first two
+//    tiles are issued as soon as the indices have landed.
 //  * QK on 16x16x32 bf16 MFMAs as S^T = K . Q^T: A = 16 tokens x 32 dims of
 //    the staged tile (fp8 -> bf16 in registers), B = Q^T, loaded once per
 //    piece into accumulation registers (the 48-row block keeps the last
-//    dims in LDS instead, so that O and Q fit the register file).  Wave w
-//    owns token quarter w of every tile for all row groups, so each staged
+//    256 dims in LDS instead, so that O and Q fit the register file).  Wave
+//    w owns token quarter w of every tile for all row groups, so each staged
 //    byte is converted to bf16 once per block.
-//  * Softmax: base-2 online softmax against a lazy per-row reference: P =
-//    2^(x - ref) is kept in bf16 with f32 sums, so the reference only moves
-//    (and O is only rescaled, outside the hot loop) when a row's maximum
-//    exceeds it by more than 2^64; per-tile row maxima are exchanged through
-//    LDS so every wave uses the same reference.  Two barriers per tile: the
-//    max exchange, and "P^T written + next tile landed" (tiles are triple
-//    buffered, so the load of tile i+2 overlaps tiles i and i+1).
+//  * Softmax: base-2, against a lazy per-row reference shared by the four
+//    waves: P = 2^(s*c - ref) in bf16, sums in f32.  One barrier per tile:
+//    each wave computes P optimistically and flags scores above its row's
+//    threshold (reference + 64); the flags travel with P^T and are read
+//    after the barrier.  A flagged tile (a piece's first, in practice)
+//    exchanges the quarter maxima; a row that outgrew its reference by more
+//    than 2^64 restarts the piece with the new one, so O is never rescaled.
 //  * PV as O^T = V^T . P^T: wave w owns latent columns [128w, 128w+128).
 //    The A operand (8 tokens of one column) comes straight from the
 //    staged tile with ds_read_b64_tr_b8; the B operand is P^T, written to
 //    LDS by the S-tile owners directly in MFMA operand order (the S^T
 //    accumulator layout gives each lane 4 consecutive tokens, so the PV
 //    contraction uses the matching token permutation).
+//  * Epilogue: O is normalised into LDS as bf16 rows and written out one
+//    whole 1 KB row per store instruction.
 #include "common.hpp"
 
 namespace mla {
 
 constexpr int NT = 64;             // tokens per tile
 constexpr int TILE_BYTES = 36864;  // one staged tile: 36 blocks of 1 KB
-constexpr float kLazy = 64.0f;  // rebase threshold, log2 units (P <= 2^64 in bf16 / f32 sums)
+constexpr float kLazy = 64.0f;  // restart threshold, log2 units (P <= 2^64 in bf16 / f32 sums)
 
 struct PartialArgs {
   const uint16_t* q;
@@ -463,7 +466,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
-  __shared__ __attribute__((aligned(16))) int32_t redflag[8];          // rebase requests, by tile parity
+  __shared__ __attribute__((aligned(16))) int32_t redflag[8];          // reference flags, by tile parity
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
@@ -717,10 +720,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       // One barrier per tile.  Each wave computes its quarter's scores and
       // P against the shared reference optimistically and flags the rows
       // that need a new one: a row's first finite maximum (its reference is
-      // set, nothing to rescale), or a maximum that outgrew the reference by
-      // more than 2^64 (rare: the loop is left to rescale O, the only place
-      // O is touched outside the MFMAs).  The flags are block-uniform after
-      // the barrier, since every wave reads the same exchanged maxima.
+      // set), or a maximum that outgrew the reference by more than 2^64
+      // (rare: the piece restarts with the new reference).  The decisions
+      // are block-uniform after the barrier, since every wave reads the same
+      // flags and the same exchanged maxima.
       for (int it = 0; it < ntiles; ++it) {
         const int t0 = s0 + NT * it;
         const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
