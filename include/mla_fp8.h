@@ -48,6 +48,11 @@ extern "C" {
 #define MLA_D_QK 576     /* one cache row: 512 latent then 64 rope   */
 #define MLA_D_V 128      /* v_head_dim: W_UV output width per head    */
 
+/* Partition weight: in the token stream the split partition cuts, each
+ * request takes this many positions before its tokens, so that units which
+ * start more pieces (each with a fixed start-up cost) get fewer tokens. */
+#define MLA_PIECE_TOKENS 320
+
 #define MLA_W_BF16 0
 #define MLA_W_MXFP4 1
 
@@ -86,14 +91,18 @@ int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe
  * For head h < heads, over a token range [a, b) of the row's visible tokens:
  *   s_i = sm_scale * kv_scale * sum_{d<576} q[t][h][d] * fp8(kv[row_i][d])
  *   LSE = ln sum_i exp(s_i),   o = kv_scale * sum_i exp(s_i - LSE) * fp8(kv[row_i][0:512])
- * The ranges are the splits: the KV token stream (kv_indices order) is cut
- * every `chunk` tokens,
- *   chunk = max(split_min_tokens, ceil(T / num_workers), ceil(L_max / (num_splits-1)))
- *   (chunk = max(split_min_tokens, T) when num_splits == 1),
- * T the total and L_max the longest request; split k of request r is its
- * k-th piece between cuts (mla_split_plan computes the same partition on
- * the host).  One workgroup set processes one chunk, so the work is token
- * balanced across num_workers workers.
+ * The ranges are the splits.  In a stream where request r (kv_indices
+ * order) takes MLA_PIECE_TOKENS positions followed by its L_r tokens (its
+ * first token at V_r = kv_indptr[r] - kv_indptr[0] + MLA_PIECE_TOKENS*(r+1)),
+ * of length T_v = T + MLA_PIECE_TOKENS*batch, a cut falls every `chunk`
+ * positions,
+ *   chunk = max(split_min_tokens, ceil(T_v / num_workers), ceil(L_max / (num_splits-1)))
+ *   (chunk = max(split_min_tokens, T_v) when num_splits == 1),
+ * T the total tokens and L_max the longest request; split k of request r is
+ * its k-th piece between cuts (mla_split_plan computes the same partition
+ * on the host).  One workgroup set processes one chunk, so the work, counted
+ * as tokens plus a fixed cost per piece, is balanced across num_workers
+ * workers.
  *
  * Outputs, for every k < num_splits, t < S, h < heads:
  *   lse_part[k*ls_split + t*ls_row + h*ls_head]          f32, -inf if split k is

@@ -93,8 +93,9 @@ __device__ __forceinline__ float nan_max(float a, float b) {
 // ------------------------------------------------------------ split plan
 
 // The split partition of mla_decode_partial, shared by the device kernel
-// and the host helper: `chunk` from the token total T, the longest request
-// and the caller's bounds.
+// and the host helper: `chunk` from the partition stream's length T (the
+// tokens plus MLA_PIECE_TOKENS per request), the longest request and the
+// caller's bounds.
 __host__ __device__ __forceinline__ int64_t split_chunk(int64_t T, int64_t lmax, int32_t num_splits,
                                                         int32_t num_workers, int32_t split_min) {
   int64_t chunk = split_min > 1 ? split_min : 1;

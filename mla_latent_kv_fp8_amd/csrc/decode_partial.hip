@@ -528,11 +528,14 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   __syncthreads();
   lmax = max(max(red_i[0], red_i[1]), max(red_i[2], red_i[3]));
   const int base = ip(0);
-  const int64_t T = (int64_t)ip(p.batch) - base;
-  const int64_t chunk = split_chunk(T, lmax, p.num_splits, p.num_workers, p.split_min);
-  const int64_t nunits = T > 0 ? (T + chunk - 1) / chunk : 1;
+  // the partition's stream: request r takes MLA_PIECE_TOKENS positions, then
+  // its tokens; Vs(r) = ip(r) - base + W r is where it starts
+  constexpr int64_t W = MLA_PIECE_TOKENS;
+  const int64_t Tv = (int64_t)ip(p.batch) - base + W * p.batch;
+  const int64_t chunk = split_chunk(Tv, lmax, p.num_splits, p.num_workers, p.split_min);
+  const int64_t nunits = Tv > 0 ? (Tv + chunk - 1) / chunk : 1;
   const int64_t g0 = (int64_t)u * chunk;
-  const int64_t g1 = g0 + chunk < T ? g0 + chunk : T;
+  const int64_t g1 = g0 + chunk < Tv ? g0 + chunk : Tv;
   const bool last_unit = (u == nunits - 1);
   const int m_lo = rb * RB;  // first row (of the request's qlen*heads) of this block
 
@@ -542,13 +545,13 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     int lo = 0, hi = p.batch;
     while (lo < hi) {
       int mid = (lo + hi) >> 1;
-      if ((int64_t)ip(mid + 1) - base >= g0) hi = mid; else lo = mid + 1;
+      if ((int64_t)ip(mid + 1) - base + W * (mid + 1) >= g0) hi = mid; else lo = mid + 1;
     }
     r = lo;
     r_end = r;
     while (r_end < p.batch) {
-      const int64_t P = (int64_t)ip(r_end) - base;
-      if (P >= g1 && !(last_unit && P == T)) break;
+      const int64_t Vs = (int64_t)ip(r_end) - base + W * r_end;
+      if (Vs >= g1 && !(last_unit && Vs == Tv)) break;
       ++r_end;
     }
   }
@@ -595,17 +598,18 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
       P = (int64_t)p.indptr[r] - base;
       L = p.indptr[r + 1] - p.indptr[r];
     }
+    const int64_t V = P + W * (r + 1);  // stream position of the request's first token
     if (L == 0) {
-      const int64_t owner = P / chunk < nunits - 1 ? P / chunk : nunits - 1;
+      const int64_t owner = V / chunk < nunits - 1 ? V / chunk : nunits - 1;
       if (owner == u) fill_neginf(r, 0);
       continue;
     }
-    const int a = (int)((g0 > P ? g0 : P) - P);
-    const int b = (int)((g1 < P + L ? g1 : P + L) - P);
+    const int a = (int)((g0 > V ? g0 : V) - V);
+    const int b = (int)((g1 < V + L ? g1 : V + L) - V);
     if (b <= a) continue;
-    const int k = (a == 0) ? 0 : (int)((P + a) / chunk - P / chunk);
+    const int k = (a == 0) ? 0 : (int)((V + a) / chunk - V / chunk);
     if (k == 0) {
-      const int nsplit = (int)((P + L - 1) / chunk - P / chunk + 1);
+      const int nsplit = (int)((V + L - 1) / chunk - V / chunk + 1);
       if (nsplit < p.num_splits) fill_neginf(r, nsplit);
     }
 
@@ -883,21 +887,23 @@ extern "C" int mla_split_plan(const int32_t* indptr, int32_t batch, int32_t num_
                               int32_t num_workers, int32_t split_min_tokens, int32_t* bounds,
                               int64_t* chunk_out) {
   if (!indptr || !bounds || batch < 0 || num_splits < 1 || num_workers < 1) return MLA_ERR_INVALID;
+  constexpr int64_t W = MLA_PIECE_TOKENS;
   int64_t T = (int64_t)indptr[batch] - indptr[0], lmax = 0;
   for (int r = 0; r < batch; ++r) {
     int64_t L = (int64_t)indptr[r + 1] - indptr[r];
     if (L < 0) return MLA_ERR_INVALID;
     if (L > lmax) lmax = L;
   }
-  const int64_t chunk = mla::split_chunk(T, lmax, num_splits, num_workers, split_min_tokens);
+  const int64_t chunk = mla::split_chunk(T + W * batch, lmax, num_splits, num_workers, split_min_tokens);
   for (int r = 0; r < batch; ++r) {
-    const int64_t P = (int64_t)indptr[r] - indptr[0], L = (int64_t)indptr[r + 1] - indptr[r];
+    const int64_t L = (int64_t)indptr[r + 1] - indptr[r];
+    const int64_t V = (int64_t)indptr[r] - indptr[0] + W * (r + 1);  // first token's stream position
     int32_t* b = bounds + (int64_t)r * (num_splits + 1);
     int k = 0;
     b[k++] = 0;
-    for (int64_t c = (P / chunk + 1) * chunk; c < P + L; c += chunk) {
+    for (int64_t c = (V / chunk + 1) * chunk; c < V + L; c += chunk) {
       if (k >= num_splits) return MLA_ERR_INVALID;
-      b[k++] = (int32_t)(c - P);
+      b[k++] = (int32_t)(c - V);
     }
     while (k <= num_splits) b[k++] = (int32_t)L;
   }

@@ -146,6 +146,11 @@ def kv_write(kv_c, k_pe, slot_mapping, kv_cache, kv_scale: float) -> np.ndarray:
     return out
 
 
+# stream positions each request takes before its tokens in the split
+# partition (the C oracle's ORC_PIECE_TOKENS)
+PIECE_TOKENS = 320
+
+
 def split_bounds(indptr, num_splits: int, num_workers: int, split_min_tokens: int):
     """Split-KV partition: returns (bounds [batch, num_splits+1] int32, chunk)."""
     indptr = _c(indptr, np.int32)

@@ -154,20 +154,24 @@ static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 /* Split-KV partition.  [MLA] `m1c_inputs` gives only the shape of the
  * partials, o [splits, S, H, 512] and LSE [splits, S, H].  Reading taken:
- * the concatenated KV token stream (the order of kv_indices) is cut every
- * `chunk` tokens, with
- *   chunk = max(split_min_tokens, ceil(T / num_workers),
+ * a stream in which request r takes ORC_PIECE_TOKENS positions followed by
+ * its L_r tokens (in kv_indices order) is cut every `chunk` positions, with
+ *   T_v   = T + ORC_PIECE_TOKENS * batch
+ *   chunk = max(split_min_tokens, ceil(T_v / num_workers),
  *               ceil(L_max / (num_splits - 1)))   (num_splits > 1)
- *   chunk = max(1, T)                              (num_splits == 1)
+ *   chunk = max(1, T_v)                            (num_splits == 1)
  * where T is the total number of tokens and L_max the longest request.  A
  * request's splits are its pieces between consecutive cuts, in order; the
  * third term keeps every request within num_splits pieces.  bounds[r][k] is
  * the first token (within request r) of split k; bounds[r][num_splits] =
  * L_r and unused splits are empty (bounds equal to L_r).
  * Returns chunk. */
+#define ORC_PIECE_TOKENS 320
+
 int64_t orc_split_bounds(const int32_t* indptr, int32_t batch, int32_t num_splits,
                          int32_t num_workers, int32_t split_min_tokens, int32_t* bounds) {
   int64_t T = (int64_t)indptr[batch] - indptr[0];
+  int64_t Tv = T + (int64_t)ORC_PIECE_TOKENS * batch;
   int64_t lmax = 0;
   for (int32_t r = 0; r < batch; ++r) {
     int64_t L = (int64_t)indptr[r + 1] - indptr[r];
@@ -175,21 +179,22 @@ int64_t orc_split_bounds(const int32_t* indptr, int32_t batch, int32_t num_split
   }
   int64_t chunk = split_min_tokens > 1 ? split_min_tokens : 1;
   if (num_splits > 1) {
-    int64_t a = num_workers > 0 ? ceil_div64(T, num_workers) : T;
+    int64_t a = num_workers > 0 ? ceil_div64(Tv, num_workers) : Tv;
     int64_t b = ceil_div64(lmax, num_splits - 1);
     if (a > chunk) chunk = a;
     if (b > chunk) chunk = b;
   } else {
-    if (T > chunk) chunk = T;
+    if (Tv > chunk) chunk = Tv;
   }
   for (int32_t r = 0; r < batch; ++r) {
-    int64_t P = (int64_t)indptr[r] - indptr[0];
+    /* V: stream position of request r's first token */
+    int64_t V = (int64_t)indptr[r] - indptr[0] + (int64_t)ORC_PIECE_TOKENS * (r + 1);
     int64_t L = (int64_t)indptr[r + 1] - indptr[r];
     int32_t* b = bounds + (int64_t)r * (num_splits + 1);
     int k = 0;
     b[k++] = 0;
-    /* every multiple of chunk strictly inside (P, P + L) starts a split */
-    for (int64_t c = (P / chunk + 1) * chunk; c < P + L; c += chunk) b[k++] = (int32_t)(c - P);
+    /* every multiple of chunk strictly inside (V, V + L) starts a split */
+    for (int64_t c = (V / chunk + 1) * chunk; c < V + L; c += chunk) b[k++] = (int32_t)(c - V);
     while (k <= num_splits) b[k++] = (int32_t)L;
   }
   return chunk;

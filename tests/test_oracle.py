@@ -154,6 +154,18 @@ def test_split_bounds_tiny_worked_example(oracle):
     assert np.array_equal(b, want)
 
 
+def test_split_bounds_weighted_worked_example(oracle):
+    """A worked example where the per-request stream positions move the cuts
+    (tests/golden/split_bounds_weighted.txt, derived by hand)."""
+    lens = [100, 0, 250]
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    b, chunk = oracle.split_bounds(indptr, 4, 4, 1)
+    lines = [l for l in open(os.path.join(GOLDEN, "split_bounds_weighted.txt")) if l[0] != "#"]
+    want = np.array([[int(v) for v in l.split(":")[1].split()] for l in lines], dtype=np.int32)
+    assert chunk == 328
+    assert np.array_equal(b, want)
+
+
 @pytest.mark.parametrize("lens,ns,W,mn", [
     ([1024, 8192, 0, 4000, 17], 16, 256, 256),
     ([5, 0, 0, 9], 3, 4, 1),
@@ -170,7 +182,8 @@ def test_split_bounds_properties(oracle, lens, ns, W, mn):
     for r, L in enumerate(lens):
         br = b[r]
         assert br[0] == 0 and br[-1] == L and (np.diff(br) >= 0).all()
-        P = int(indptr[r])
+        # stream position of the request's first token
+        P = int(indptr[r]) + oracle.PIECE_TOKENS * (r + 1)
         for k in range(ns):
             lo, hi = int(br[k]), int(br[k + 1])
             if hi > lo:
