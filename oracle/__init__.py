@@ -66,6 +66,8 @@ def lib():
         L.orc_split_bounds.restype = i64
         L.orc_decode_partial.argtypes = [P, i32, i32, i32, P, P, P, P, i32, f64, f64, P, P]
         L.orc_decode_partial.restype = None
+        L.orc_decode_partial_q8.argtypes = [P, f64, i32, i32, i32, P, P, P, P, i32, f64, f64, P, P]
+        L.orc_decode_partial_q8.restype = None
         L.orc_merge_lse.argtypes = [P, P, i32, i64, i32, P, P]
         L.orc_merge_lse.restype = None
         L.orc_value_gate.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
@@ -160,10 +162,14 @@ def split_bounds(indptr, num_splits: int, num_workers: int, split_min_tokens: in
     return b, int(chunk)
 
 
-def decode_partial(q, kv_cache, indptr, indices, bounds, qlen: int, sm_scale: float, kv_scale: float):
-    """Exact split partials.  q [S, H, 576] bf16 bits.  Returns (o f64
-    [splits, S, H, 512], lse f64 [splits, S, H]); o is NOT rounded."""
-    q = _c(q, np.uint16)
+def decode_partial(q, kv_cache, indptr, indices, bounds, qlen: int, sm_scale: float, kv_scale: float,
+                   q_scale: float | None = None):
+    """Exact split partials.  q [S, H, 576]: bf16 bits (uint16), or fp8 E4M3
+    codes (uint8) standing for q_scale * D(q8) when q_scale is given.
+    Returns (o f64 [splits, S, H, 512], lse f64 [splits, S, H]); o is NOT
+    rounded."""
+    fp8_q = q_scale is not None
+    q = _c(q, np.uint8 if fp8_q else np.uint16)
     S, H, D = q.shape
     assert D == D_QK
     kv = _c(kv_cache, np.uint8)
@@ -175,8 +181,12 @@ def decode_partial(q, kv_cache, indptr, indices, bounds, qlen: int, sm_scale: fl
     ns = bounds.shape[1] - 1
     o = np.empty((ns, S, H, D_LATENT), dtype=np.float64)
     lse = np.empty((ns, S, H), dtype=np.float64)
-    lib().orc_decode_partial(_p(q), batch, qlen, H, _p(kv), _p(indptr), _p(indices), _p(bounds), ns,
-                             float(sm_scale), float(kv_scale), _p(o), _p(lse))
+    if fp8_q:
+        lib().orc_decode_partial_q8(_p(q), float(q_scale), batch, qlen, H, _p(kv), _p(indptr), _p(indices),
+                                    _p(bounds), ns, float(sm_scale), float(kv_scale), _p(o), _p(lse))
+    else:
+        lib().orc_decode_partial(_p(q), batch, qlen, H, _p(kv), _p(indptr), _p(indices), _p(bounds), ns,
+                                 float(sm_scale), float(kv_scale), _p(o), _p(lse))
     return o, lse
 
 

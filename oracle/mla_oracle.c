@@ -203,11 +203,12 @@ int64_t orc_split_bounds(const int32_t* indptr, int32_t batch, int32_t num_split
 /* ----------------------------------------------------- attention (exact) */
 
 /* Exact softmax attention of one query row of one head over tokens
- * [lo, hi) of request r (definition behind [MLA] `attend` / `m1c_inputs`):
+ * [lo, hi) of request r (definition behind [MLA] `attend` / `m1c_inputs`),
+ * with the query row already decoded to real values q[d]:
  *   s_i = sm_scale * kv_scale * sum_{d<576} q[d] * D(kv[row_i][d])
  *   LSE = ln sum_i exp(s_i),   o = kv_scale * sum_i exp(s_i - LSE) * D(kv[row_i][0:512])
  * An empty range gives LSE = -inf and o = 0. */
-static void attend_row(const uint16_t* qrow, const uint8_t* kv_cache, const int32_t* rows,
+static void attend_row(const double* qd, const uint8_t* kv_cache, const int32_t* rows,
                        int64_t lo, int64_t hi, double sm_scale, double kv_scale, double* s,
                        double* lse_out, double* o_out) {
   for (int d = 0; d < ORC_D_LATENT; ++d) o_out[d] = 0.0;
@@ -215,8 +216,6 @@ static void attend_row(const uint16_t* qrow, const uint8_t* kv_cache, const int3
     *lse_out = -INFINITY;
     return;
   }
-  double qd[ORC_D_QK];
-  for (int d = 0; d < ORC_D_QK; ++d) qd[d] = orc_bf16_decode(qrow[d]);
   double m = -INFINITY;
   for (int64_t i = lo; i < hi; ++i) {
     const uint8_t* kr = kv_cache + (int64_t)rows[i] * ORC_D_QK;
@@ -237,6 +236,18 @@ static void attend_row(const uint16_t* qrow, const uint8_t* kv_cache, const int3
   *lse_out = lse;
 }
 
+/* The query of row t, head h as real values: a bf16 query is its bf16
+ * value; an fp8 query (q8 of [MLA] `pre`, the query quantised with the
+ * per-tensor scale q_scale, which `attend` hands to the decode as is) is
+ * q_scale * D(q8), D the E4M3 decode above.  Reading taken: the quantised
+ * query stands for q_scale times its decoded value, as the cache row stands
+ * for kv_scale times its own. */
+static void decode_query(const void* q, int q_fp8, double q_scale, int64_t off, double* qd) {
+  for (int d = 0; d < ORC_D_QK; ++d)
+    qd[d] = q_fp8 ? q_scale * orc_fp8_decode(((const uint8_t*)q)[off + d])
+                  : orc_bf16_decode(((const uint16_t*)q)[off + d]);
+}
+
 /* Split-KV partial attention ([MLA] `m1c_inputs`: o [splits, S, H, 512]
  * and LSE [splits, S, H]).  q is [S, H, 576] contiguous with S = batch*qlen;
  * row t = r*qlen + j belongs to request r.  Reading taken for qlen > 1 (the
@@ -246,10 +257,10 @@ static void attend_row(const uint16_t* qrow, const uint8_t* kv_cache, const int3
  * the exact attention over [bounds[r][k], bounds[r][k+1]) intersected with
  * the visible prefix; o_out / lse_out are [num_splits][S][H][512] / [..][H]
  * in double (rounding o to bf16 is a separate step). */
-void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t heads,
-                        const uint8_t* kv_cache, const int32_t* indptr, const int32_t* indices,
-                        const int32_t* bounds, int32_t num_splits, double sm_scale,
-                        double kv_scale, double* o_out, double* lse_out) {
+static void decode_partial(const void* q, int q_fp8, double q_scale, int32_t batch, int32_t qlen,
+                           int32_t heads, const uint8_t* kv_cache, const int32_t* indptr,
+                           const int32_t* indices, const int32_t* bounds, int32_t num_splits,
+                           double sm_scale, double kv_scale, double* o_out, double* lse_out) {
   int64_t S = (int64_t)batch * qlen;
   int64_t lmax = 0;
   for (int32_t r = 0; r < batch; ++r)
@@ -258,6 +269,7 @@ void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t 
 #pragma omp parallel
   {
     double* s = (double*)malloc(sizeof(double) * (size_t)(lmax > 0 ? lmax : 1));
+    double qd[ORC_D_QK];
 #pragma omp for schedule(dynamic, 1)
     for (int64_t w = 0; w < total; ++w) {
       int64_t h = w % heads;
@@ -271,11 +283,31 @@ void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t 
       int64_t lo = b[k], hi = b[k + 1];
       if (hi > visible) hi = visible;
       const int32_t* rows = indices + indptr[r];
-      attend_row(q + (t * heads + h) * ORC_D_QK, kv_cache, rows, lo, hi, sm_scale, kv_scale, s,
-                 lse_out + (k * S + t) * heads + h, o_out + ((k * S + t) * heads + h) * ORC_D_LATENT);
+      decode_query(q, q_fp8, q_scale, (t * heads + h) * ORC_D_QK, qd);
+      attend_row(qd, kv_cache, rows, lo, hi, sm_scale, kv_scale, s, lse_out + (k * S + t) * heads + h,
+                 o_out + ((k * S + t) * heads + h) * ORC_D_LATENT);
     }
     free(s);
   }
+}
+
+/* bf16 query [S, H, 576] (the bf16 query of [MLA] `m1c_inputs`). */
+void orc_decode_partial(const uint16_t* q, int32_t batch, int32_t qlen, int32_t heads,
+                        const uint8_t* kv_cache, const int32_t* indptr, const int32_t* indices,
+                        const int32_t* bounds, int32_t num_splits, double sm_scale,
+                        double kv_scale, double* o_out, double* lse_out) {
+  decode_partial(q, 0, 1.0, batch, qlen, heads, kv_cache, indptr, indices, bounds, num_splits, sm_scale,
+                 kv_scale, o_out, lse_out);
+}
+
+/* fp8 E4M3 query q8 [S, H, 576] with its per-tensor scale ([MLA] `pre`
+ * returns it, `attend` decodes with it). */
+void orc_decode_partial_q8(const uint8_t* q8, double q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                           const uint8_t* kv_cache, const int32_t* indptr, const int32_t* indices,
+                           const int32_t* bounds, int32_t num_splits, double sm_scale,
+                           double kv_scale, double* o_out, double* lse_out) {
+  decode_partial(q8, 1, q_scale, batch, qlen, heads, kv_cache, indptr, indices, bounds, num_splits,
+                 sm_scale, kv_scale, o_out, lse_out);
 }
 
 /* -------------------------------------------------------------- merge */

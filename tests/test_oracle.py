@@ -208,9 +208,10 @@ def _bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(torch.float64)
 
 
-def _sdpa_reference(q_bits, kv_bytes, indptr, indices, qlen, sm_scale, kv_scale):
+def _sdpa_reference(q_bits, kv_bytes, indptr, indices, qlen, sm_scale, kv_scale, q_real=None):
     """Library attention: torch SDPA (float64, CPU) with a boolean causal
-    window mask, and torch.logsumexp for the LSE."""
+    window mask, and torch.logsumexp for the LSE.  q_real (float64
+    [S, H, 576]) replaces the bf16 query when given."""
     S, H, _ = q_bits.shape
     B = len(indptr) - 1
     o = np.zeros((S, H, 512))
@@ -221,7 +222,10 @@ def _sdpa_reference(q_bits, kv_bytes, indptr, indices, qlen, sm_scale, kv_scale)
             continue
         rows = indices[indptr[r]:indptr[r + 1]]
         kv = _decode_kv(kv_bytes[rows])           # [L, 576]
-        q = _bf16(q_bits[r * qlen:(r + 1) * qlen])  # [qlen, H, 576]
+        if q_real is None:
+            q = _bf16(q_bits[r * qlen:(r + 1) * qlen])  # [qlen, H, 576]
+        else:
+            q = torch.from_numpy(np.ascontiguousarray(q_real[r * qlen:(r + 1) * qlen]))
         vis = torch.tensor([[i < L - qlen + j + 1 for i in range(L)] for j in range(qlen)])
         qq = q.permute(1, 0, 2).unsqueeze(0)       # [1, H, qlen, 576]
         k = kv.unsqueeze(0).unsqueeze(0)           # [1, 1, L, 576]
@@ -323,6 +327,77 @@ def test_causal_window_rows_see_prefix(oracle):
                                        1, sm, 1.0)
         np.testing.assert_array_equal(o1[0, 0], o[0, j])
         np.testing.assert_array_equal(l1[0, 0], lse[0, j])
+
+
+# --------------------------------------------------- fp8 query (q8, q_scale)
+
+def _q8_codes(rng, shape, std=16.0):
+    """E4M3 codes of N(0, std^2) draws by torch's cast (all finite: the draws
+    stay far below the format's 448)."""
+    x = torch.from_numpy(rng.standard_normal(shape).astype(np.float32) * np.float32(std))
+    return x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("lens,H,qlen,q_scale", [
+    ([37, 64], 16, 1, 0.0625),
+    ([5, 1, 0, 33], 3, 1, 0.03),
+    ([9, 16, 4], 2, 4, 0.07),
+])
+def test_attention_q8_matches_library_sdpa(oracle, lens, H, qlen, q_scale):
+    # the fp8 query stands for q_scale * D(q8): torch's fp8 decode times the
+    # scale, then torch SDPA
+    rng = np.random.default_rng(len(lens) * 10 + H)
+    _, kv, indptr, indices = _tiny_problem(rng, lens, H, qlen, 0.05)
+    q8 = _q8_codes(rng, (len(lens) * qlen, H, 576))
+    sm = 1 / math.sqrt(192)
+    b, _ = oracle.split_bounds(indptr, 1, 1, 1)
+    o, lse = oracle.decode_partial(q8, kv, indptr, indices, b, qlen, sm, 0.05, q_scale=q_scale)
+    q_real = _decode_kv(q8).numpy() * q_scale
+    ro, rl = _sdpa_reference(q8, kv, indptr, indices, qlen, sm, 0.05, q_real=q_real)
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse[0]), fin)
+    np.testing.assert_allclose(lse[0][fin], rl[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0][fin], ro[fin], rtol=0, atol=1e-12)
+
+
+def test_q8_power_of_two_scale_is_the_bf16_query(oracle):
+    # 2^-4 * D(code) has at most 4 significant bits: it is exactly a bf16
+    # value, and the fp8 query must give bit-identical partials to that bf16
+    # query (the query decode is the only difference between the two paths)
+    rng = np.random.default_rng(11)
+    _, kv, indptr, indices = _tiny_problem(rng, [21, 0, 40], 5, 2, 0.05)
+    q8 = _q8_codes(rng, (6, 5, 576))
+    real = (_decode_kv(q8).numpy() * 0.0625).astype(np.float32)
+    w = real.view(np.uint32)
+    assert (w & 0xFFFF == 0).all()
+    qb = (w >> 16).astype(np.uint16)
+    b, _ = oracle.split_bounds(indptr, 3, 1, 8)
+    o8, l8 = oracle.decode_partial(q8, kv, indptr, indices, b, 2, 0.08, 0.05, q_scale=0.0625)
+    ob, lb = oracle.decode_partial(qb, kv, indptr, indices, b, 2, 0.08, 0.05)
+    np.testing.assert_array_equal(o8, ob)
+    np.testing.assert_array_equal(l8, lb)
+    # a scale that is not a power of two multiplies every score: the same as
+    # the unscaled query with sm_scale * q_scale
+    real1 = _decode_kv(q8).numpy().astype(np.float32)
+    qb1 = (real1.view(np.uint32) >> 16).astype(np.uint16)
+    o3, l3 = oracle.decode_partial(q8, kv, indptr, indices, b, 2, 0.08, 0.05, q_scale=0.03)
+    o1, l1 = oracle.decode_partial(qb1, kv, indptr, indices, b, 2, 0.08 * 0.03, 0.05)
+    fin = np.isfinite(l1)
+    assert np.array_equal(np.isfinite(l3), fin)
+    np.testing.assert_allclose(l3[fin], l1[fin], rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o3, o1, rtol=0, atol=1e-13)
+
+
+def test_q8_zero_query_closed_form(oracle):
+    # q8 = 0: every score is 0, so LSE = ln n and o = kv_scale * mean(v)
+    rng = np.random.default_rng(12)
+    _, kv, indptr, indices = _tiny_problem(rng, [13], 2, 1, 0.25)
+    q8 = np.zeros((1, 2, 576), dtype=np.uint8)
+    o, lse = oracle.decode_partial(q8, kv, indptr, indices, oracle.split_bounds(indptr, 1, 1, 1)[0], 1,
+                                   0.1, 0.25, q_scale=0.5)
+    v = oracle.fp8_decode(kv[indices])[:, :512]
+    np.testing.assert_allclose(lse[0, 0], np.log(13), atol=1e-14)
+    np.testing.assert_allclose(o[0, 0, 1], 0.25 * v.mean(0), atol=1e-14)
 
 
 def _merge_f64(o, lse):
