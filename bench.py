@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="batch")
+    ap.add_argument("--fp8-query", action="store_true",
+                    help="run the partials on an fp8 E4M3 query with a per-tensor scale "
+                         "(mla_decode_partial_fp8q) instead of the bf16 query")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -149,6 +152,9 @@ def main():
     print("[bench] workload %s: B=%d qlen=%d H=%d tokens=%d" % (w.name, w.batch, w.qlen, w.heads, w.total_tokens),
           file=sys.stderr, flush=True)
     st = DeviceStep(w)
+    if args.fp8_query:
+        q8, q_scale = synth.fp8_query(np.random.default_rng(w.seed + 77), w.q.shape, w.heads)
+        st.q, st.q_scale = torch.from_numpy(q8).to(st.dev), q_scale
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
@@ -215,16 +221,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 KV, bf16 MFMA (f32 accumulate)",
+        "dtype": "fp8-e4m3 KV%s, bf16 MFMA (f32 accumulate)" % (" and query" if args.fp8_query else ""),
         "data": "synthetic (seeded; no dataset or weights)",
-        "config": {"workload": "%s: B=%d qlen=%d heads=%d (query buffer %d) tokens=%d kv_scale=%g splits<=%d "
-                               "workers=%d W_UV=%s" % (w.name, w.batch, w.qlen, w.heads, w.heads_pad,
-                                                         w.total_tokens, w.kv_scale, w.num_splits,
-                                                         w.num_workers, w.w_format),
+        "config": {"workload": "%s: B=%d qlen=%d heads=%d (query buffer %d%s) tokens=%d kv_scale=%g "
+                               "splits<=%d workers=%d W_UV=%s" % (w.name, w.batch, w.qlen, w.heads, w.heads_pad,
+                                                                  ", fp8 E4M3 + per-tensor scale" if args.fp8_query
+                                                                  else " bf16", w.total_tokens, w.kv_scale,
+                                                                  w.num_splits, w.num_workers, w.w_format),
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(args.config),
+                     "traffic": None if args.fp8_query else measured_traffic(args.config),
                      "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
                      "flops_per_launch": flops},
         "roofline_hbm": {"achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

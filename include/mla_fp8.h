@@ -10,6 +10,7 @@
  *   mla_kv_write        new tokens' [kv_c | k_pe] rows -> fp8 cache rows
  *   mla_decode_partial  absorbed queries attend over the paged fp8 cache:
  *                       split-KV partials o (bf16) and LSE (f32)
+ *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
  *
@@ -121,6 +122,28 @@ int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride
                        int32_t split_min_tokens, uint16_t* o_part, int64_t os_split, int64_t os_row,
                        int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row,
                        int64_t ls_head, void* stream);
+
+/*
+ * The same split-KV partials for an fp8 query ([MLA] `pre` quantises the
+ * absorbed query to fp8 E4M3 with one per-tensor scale, and `attend` decodes
+ * on that quantised query).  Query element d of row t, head h stands for
+ *   q_scale * fp8(q8[t][h][d]),
+ * so every score is the bf16-query formula above with q replaced by that
+ * value:  s_i = sm_scale * kv_scale * q_scale * sum_d fp8(q8) * fp8(kv).
+ * Everything else (rows, causal rule, split partition, outputs, errors) is
+ * as for mla_decode_partial.
+ *   q8       [S][...][576] u8 E4M3 codes, strides (q_stride_row,
+ *            q_stride_head) in bytes, both multiples of 16, q8 16-byte
+ *            aligned (otherwise MLA_ERR_UNSUPPORTED)
+ *   q_scale  > 0 and finite (otherwise MLA_ERR_INVALID)
+ */
+int mla_decode_partial_fp8q(const uint8_t* q8, int64_t q_stride_row, int64_t q_stride_head, float q_scale,
+                            int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
+                            int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
+                            float sm_scale, float kv_scale, int32_t num_splits, int32_t num_workers,
+                            int32_t split_min_tokens, uint16_t* o_part, int64_t os_split,
+                            int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split,
+                            int64_t ls_row, int64_t ls_head, void* stream);
 
 /*
  * Host helper: the split partition mla_decode_partial uses.

@@ -43,13 +43,15 @@ def lib() -> ctypes.CDLL:
         L.mla_kv_write.argtypes = [P, i64, P, i64, P, i32, P, i64, f32, P]
         L.mla_decode_partial.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32,
                                          i32, P, i64, i64, i64, P, i64, i64, i64, P]
+        L.mla_decode_partial_fp8q.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32, f32,
+                                              i32, i32, i32, P, i64, i64, i64, P, i64, i64, i64, P]
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
         L.mla_merge_lse.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, i32, P, i64, i64, P,
                                     i64, i64, P]
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
-        for name in ("mla_kv_write", "mla_decode_partial", "mla_split_plan", "mla_merge_lse",
-                     "mla_value_gate"):
+        for name in ("mla_kv_write", "mla_decode_partial", "mla_decode_partial_fp8q", "mla_split_plan",
+                     "mla_merge_lse", "mla_value_gate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -95,11 +97,12 @@ def kv_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
 def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,
                    kv_indices: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor, *, qlen: int,
                    heads: int, sm_scale: float, kv_scale: float, num_workers: int = 256,
-                   split_min_tokens: int = 256) -> None:
-    """Split-KV partials: q [S, H_pad, 576] bf16 (first `heads` used) over
+                   split_min_tokens: int = 256, q_scale: float | None = None) -> None:
+    """Split-KV partials: q [S, H_pad, 576] (first `heads` used) over
     kv_cache [num_slots, 576] u8 with CSR (kv_indptr [B+1], kv_indices) int32
     -> o_part [splits, S, heads, 512] bf16, lse_part [splits, S, heads] f32
-    (strided views allowed)."""
+    (strided views allowed).  q is bf16, or fp8 E4M3 codes (uint8 or
+    float8_e4m3fn) standing for q_scale * fp8(q), which then must be given."""
     S = q.shape[0]
     batch = kv_indptr.shape[0] - 1
     if S != batch * qlen:
@@ -109,15 +112,21 @@ def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Ten
         raise MlaError("bad partial buffer shapes")
     if q.shape[-1] != D_QK or q.shape[1] < heads:
         raise MlaError("q must be [S, >=heads, 576]")
-    st = lib().mla_decode_partial(
-        _dev(q, "q", _BF16), q.stride(0), q.stride(1), batch, qlen, heads,
-        _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0],
-        _dev(kv_indptr, "kv_indptr", (torch.int32,)), _dev(kv_indices, "kv_indices", (torch.int32,)),
-        float(sm_scale), float(kv_scale), ns, int(num_workers), int(split_min_tokens),
-        _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
-        _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
-        lse_part.stride(2), _stream())
-    _check(st, "mla_decode_partial")
+    fp8_q = q.dtype in _U8
+    if fp8_q != (q_scale is not None):
+        raise MlaError("an fp8 query takes q_scale, a bf16 query does not")
+    rest = (batch, qlen, heads, _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0],
+            _dev(kv_indptr, "kv_indptr", (torch.int32,)), _dev(kv_indices, "kv_indices", (torch.int32,)),
+            float(sm_scale), float(kv_scale), ns, int(num_workers), int(split_min_tokens),
+            _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
+            _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
+            lse_part.stride(2), _stream())
+    if fp8_q:
+        st = lib().mla_decode_partial_fp8q(_dev(q, "q", _U8), q.stride(0), q.stride(1), float(q_scale), *rest)
+        _check(st, "mla_decode_partial_fp8q")
+    else:
+        st = lib().mla_decode_partial(_dev(q, "q", _BF16), q.stride(0), q.stride(1), *rest)
+        _check(st, "mla_decode_partial")
 
 
 def split_plan(kv_indptr, num_splits: int, num_workers: int, split_min_tokens: int):

@@ -45,14 +45,15 @@ constexpr int TILE_BYTES = 36864;  // one staged tile: 36 blocks of 1 KB
 constexpr float kLazy = 64.0f;  // restart threshold, log2 units (P <= 2^64 in bf16 / f32 sums)
 
 struct PartialArgs {
-  const uint16_t* q;
+  const uint16_t* q;   // bf16 query, or
+  const uint8_t* q8;   // fp8 E4M3 query codes (the fp8-query variant)
   int64_t q_sr, q_sh;
   int32_t batch, qlen, heads, M, n_rb;
   const uint8_t* kv;
   int64_t num_slots;
   const int32_t* indptr;
   const int32_t* indices;
-  float c_log2;  // sm_scale * kv_scale * log2(e)
+  float c_log2;  // sm_scale * kv_scale (* q_scale for an fp8 query) * log2(e)
   float kv_scale;
   int32_t num_splits, num_workers, split_min;
   uint16_t* o;
@@ -222,7 +223,12 @@ template <int NRG> constexpr int qpitch_reg() { return 16 * qw_reg<NRG>(); }
 // chunks of padding: a 544-byte pitch (48 rows) has no bank conflicts.
 template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 2); }
 
-template <int NRG>
+// An fp8 query block is staged whole, as its natural rows of 576 bytes
+// (36 chunks of 16 B) at qreg + 576 i; decode_q8 turns it into bf16 once per
+// piece.
+constexpr int Q8_PITCH = MLA_D_QK;
+
+template <int NRG, bool QF8>
 __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
                                                int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
                                                MLA_LDS int32_t* idx_lds, int wave, int lane) {
@@ -231,6 +237,29 @@ __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int 
   // the indices go first: the caller waits for them alone and issues the
   // first tiles while the query is still in flight
   stage_idx(idx_src, nidx, idx_lds, wave, lane);
+  if constexpr (QF8) {
+    constexpr int NC = RB * (Q8_PITCH / 16);
+    constexpr int NR = (NC + 63) / 64;
+    static_assert(NR * 1024 <= TILE_BYTES, "an fp8 query block is staged in one tile buffer");
+    const uint8_t* q8_base =
+        p.q8 + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
+#pragma unroll 1
+    for (int j0 = 0; j0 < NR; j0 += 4) {
+      const int j = j0 + wave;
+      if (j < NR) {
+        const int c = 64 * j + lane;
+        const int row = c / (Q8_PITCH / 16), part = c - (Q8_PITCH / 16) * row;
+        const int m = m_lo + row;
+        const uint8_t* g = q8_base;  // rows past the block or past M: the block's first row
+        if (row < RB && m < p.M) {
+          const int jj = m / p.heads, h = m - p.heads * jj;
+          g = p.q8 + (int64_t)(r * p.qlen + jj) * p.q_sr + (int64_t)h * p.q_sh + 16 * part;
+        }
+        lds_dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qreg + 1024 * j)));
+      }
+    }
+    return (NR - wave + 3) / 4;
+  }
   const uint16_t* q_base = p.q + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
   auto src_of = [&](int row, int dim8) -> const uint16_t* {
     const int m = m_lo + row;
@@ -458,7 +487,42 @@ __device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const flo
   }
 }
 
-template <int NRG>
+// fp8 query block staged at q8s (rows of Q8_PITCH bytes) -> the bf16 query
+// fragments of K-step pairs pp < QR (same dims as load order of the bf16
+// block) and, for the 48-row block, the LDS-resident dims [64 QR, 576) in
+// their read order at qlds.  E4M3 -> bf16 is exact; q_scale is folded into
+// the score constant.  The caller publishes qlds with a barrier.
+template <int NRG, int QR>
+__device__ __forceinline__ void decode_q8(const MLA_LDS uint8_t* q8s, MLA_LDS uint8_t* qlds, int tid, int lr,
+                                          int lg, bf16x8 (&qf)[NRG][2 * QR]) {
+  constexpr int RB = 16 * NRG;
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) {
+    const MLA_LDS uint8_t* src = q8s + (16 * g + lr) * Q8_PITCH + 16 * lg;
+#pragma unroll
+    for (int pp = 0; pp < QR; ++pp) {
+      const u32x4 raw = *(const MLA_LDS u32x4*)(src + 64 * pp);
+      qf[g][2 * pp] = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
+      qf[g][2 * pp + 1] = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
+    }
+  }
+  if constexpr (QR < 9) {
+    // (row, pair, lane group): 16 dims -> chunks 8p + lg (first 8) and
+    // 8p + 4 + lg (next 8) of the row's LDS part
+    constexpr int NP = 9 - QR;
+#pragma unroll 1
+    for (int e = tid; e < RB * NP * 4; e += 256) {
+      const int row = e / (NP * 4), rem = e - (NP * 4) * row;
+      const int pq = rem >> 2, l4 = rem & 3;
+      const u32x4 raw = *(const MLA_LDS u32x4*)(q8s + row * Q8_PITCH + 64 * (QR + pq) + 16 * l4);
+      MLA_LDS uint8_t* dst = qlds + row * qpitch_lds<NRG>() + 16 * (8 * pq + l4);
+      *(MLA_LDS bf16x8*)dst = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
+      *(MLA_LDS bf16x8*)(dst + 64) = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
+    }
+  }
+}
+
+template <int NRG, bool QF8>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
@@ -633,7 +697,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     // has read it).  Only the indices are waited for here: tiles 0 and 1
     // are issued while the query is still in flight.
     MLA_LDS uint8_t* qst = kbuf + 2 * TILE_BYTES;
-    const int nq = stage_q_and_idx<NRG>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
+    const int nq = stage_q_and_idx<NRG, QF8>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
     {
@@ -654,13 +718,18 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     // query fragments for K-step pairs pp < QR: K-step 2pp uses dims
     // 64pp+16lg..+7, 2pp+1 the next 8 (the K fragments use the same order)
     bf16x8 qf[NRG][2 * QR];
+    if constexpr (QF8) {
+      decode_q8<NRG, QR>(qst, qlds, tid, lr, lg, qf);
+      if constexpr (QR < 9) __syncthreads();  // the decoded LDS part is complete
+    } else {
 #pragma unroll
-    for (int g = 0; g < NRG; ++g) {
-      const MLA_LDS uint8_t* src = qst + (16 * g + lr) * qpitch_reg<NRG>() + 32 * lg;
+      for (int g = 0; g < NRG; ++g) {
+        const MLA_LDS uint8_t* src = qst + (16 * g + lr) * qpitch_reg<NRG>() + 32 * lg;
 #pragma unroll
-      for (int pp = 0; pp < QR; ++pp) {
-        qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src + 128 * pp);
-        qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src + 128 * pp + 16);
+        for (int pp = 0; pp < QR; ++pp) {
+          qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src + 128 * pp);
+          qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src + 128 * pp + 16);
+        }
       }
     }
     // keep the query fragments in AGPRs (they are only MFMA B operands), so
@@ -875,9 +944,9 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   }
 }
 
-template <int NRG>
+template <int NRG, bool QF8>
 static int launch(const PartialArgs& a, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL(partial_kernel<NRG>, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((partial_kernel<NRG, QF8>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -911,21 +980,29 @@ extern "C" int mla_split_plan(const int32_t* indptr, int32_t batch, int32_t num_
   return MLA_OK;
 }
 
-extern "C" int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
-                                  int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
-                                  int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
-                                  float sm_scale, float kv_scale, int32_t num_splits, int32_t num_workers,
-                                  int32_t split_min_tokens, uint16_t* o_part, int64_t os_split,
-                                  int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split,
-                                  int64_t ls_row, int64_t ls_head, void* stream) {
+namespace mla {
+
+// Argument checks, launch geometry and launch shared by the bf16- and
+// fp8-query entry points.  q_scale multiplies every score (1 for bf16).
+static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, int64_t q_stride_head,
+                               float q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                               const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                               const int32_t* kv_indices, float sm_scale, float kv_scale,
+                               int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                               uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                               float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                               void* stream) {
   if (batch < 0 || qlen < 1 || heads < 1 || num_splits < 1 || num_splits > 1024 || num_workers < 1)
     return MLA_ERR_INVALID;
   if (batch == 0) return MLA_OK;
   if (!q || !kv_cache || !kv_indptr || !kv_indices || !o_part || !lse_part) return MLA_ERR_INVALID;
   if (num_slots < 1 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
   if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f)) return MLA_ERR_INVALID;
-  // 16-byte query fragments, 8-byte partial stores, 16-byte cache rows
-  if ((q_stride_row | q_stride_head) % 8 != 0 || ((uintptr_t)q) % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (!(q_scale > 0.0f) || q_scale == INFINITY) return MLA_ERR_INVALID;
+  // 16-byte query chunks (8 bf16 or 16 fp8 elements), 8-byte partial
+  // stores, 16-byte cache rows
+  const int64_t q_align = q_fp8 ? 16 : 8;
+  if ((q_stride_row | q_stride_head) % q_align != 0 || ((uintptr_t)q) % 16 != 0) return MLA_ERR_UNSUPPORTED;
   if ((os_split | os_row | os_head) % 4 != 0 || ((uintptr_t)o_part) % 8 != 0) return MLA_ERR_UNSUPPORTED;
   if (((uintptr_t)kv_cache) % 16 != 0) return MLA_ERR_UNSUPPORTED;
   const int64_t M = (int64_t)qlen * heads;
@@ -936,19 +1013,57 @@ extern "C" int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64
   const int64_t blocks = (int64_t)num_workers * n_rb;
   if (blocks > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
 
-  mla::PartialArgs a;
-  a.q = q; a.q_sr = q_stride_row; a.q_sh = q_stride_head;
+  PartialArgs a;
+  a.q = q_fp8 ? nullptr : (const uint16_t*)q;
+  a.q8 = q_fp8 ? (const uint8_t*)q : nullptr;
+  a.q_sr = q_stride_row; a.q_sh = q_stride_head;
   a.batch = batch; a.qlen = qlen; a.heads = heads; a.M = (int32_t)M; a.n_rb = n_rb;
   a.kv = kv_cache; a.num_slots = num_slots; a.indptr = kv_indptr; a.indices = kv_indices;
-  a.c_log2 = sm_scale * kv_scale * mla::kLog2e;
+  a.c_log2 = sm_scale * kv_scale * q_scale * kLog2e;  // q_scale = 1: sm_scale * kv_scale * log2(e)
   a.kv_scale = kv_scale;
   a.num_splits = num_splits; a.num_workers = num_workers; a.split_min = split_min_tokens;
   a.o = o_part; a.os_s = os_split; a.os_r = os_row; a.os_h = os_head;
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
-  switch (nrg) {
-    case 1: return mla::launch<1>(a, (int)blocks, s);
-    case 2: return mla::launch<2>(a, (int)blocks, s);
-    default: return mla::launch<3>(a, (int)blocks, s);
+  if (q_fp8) {
+    switch (nrg) {
+      case 1: return launch<1, true>(a, (int)blocks, s);
+      case 2: return launch<2, true>(a, (int)blocks, s);
+      default: return launch<3, true>(a, (int)blocks, s);
+    }
   }
+  switch (nrg) {
+    case 1: return launch<1, false>(a, (int)blocks, s);
+    case 2: return launch<2, false>(a, (int)blocks, s);
+    default: return launch<3, false>(a, (int)blocks, s);
+  }
+}
+
+}  // namespace mla
+
+extern "C" int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
+                                  int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
+                                  int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  float sm_scale, float kv_scale, int32_t num_splits, int32_t num_workers,
+                                  int32_t split_min_tokens, uint16_t* o_part, int64_t os_split,
+                                  int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split,
+                                  int64_t ls_row, int64_t ls_head, void* stream) {
+  return mla::decode_partial_impl(q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
+                                  num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream);
+}
+
+extern "C" int mla_decode_partial_fp8q(const uint8_t* q8, int64_t q_stride_row, int64_t q_stride_head,
+                                       float q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                                       const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                                       const int32_t* kv_indices, float sm_scale, float kv_scale,
+                                       int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                                       uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                                       float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                                       void* stream) {
+  return mla::decode_partial_impl(q8, true, q_stride_row, q_stride_head, q_scale, batch, qlen, heads,
+                                  kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream);
 }

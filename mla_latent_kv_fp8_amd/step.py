@@ -28,6 +28,7 @@ class DeviceStep:
         self.split_min = split_min_tokens if split_min_tokens is not None else w.split_min_tokens
         S, H, VH = w.S, w.heads, w.value_heads
         self.q = _bf16_dev(w.q, dev)
+        self.q_scale = None  # set, with an fp8 self.q, for the fp8-query entry point
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
         self.indices = torch.from_numpy(w.indices).to(dev)
@@ -62,7 +63,7 @@ class DeviceStep:
         w = self.w
         decode_partial(self.q, self.kv_cache, self.indptr, self.indices, self.o_part, self.lse_part,
                        qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
-                       num_workers=self.num_workers, split_min_tokens=self.split_min)
+                       num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale)
 
     def merge(self):
         merge_lse(self.o_part, self.lse_part, self.latent[:, :self.w.heads], self.lse)

@@ -185,6 +185,19 @@ def make(name: str, seed: int | None = None, batch: int | None = None,
         extra_latent=extra_latent)
 
 
+def fp8_query(rng, shape, heads: int, std: float = 16.0) -> tuple[np.ndarray, float]:
+    """fp8 E4M3 query codes [S, H_pad, 576] of N(0, std^2) draws (torch's
+    cast, far inside the format's range) and the per-tensor scale 1/std, so
+    that the query stands for values ~ N(0, 1) like the bf16 one.  Pad heads
+    (index >= heads) hold the NaN code 0x7F: they must never be read."""
+    import torch
+
+    x = torch.from_numpy(rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std))
+    q8 = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    q8[:, heads:, :] = FP8_NAN
+    return q8, 1.0 / std
+
+
 def random_partials(rng, num_splits, rows, heads, p_empty=0.3):
     """Synthetic split partials for testing a merge on its own: bf16 o
     [splits, rows, heads, 512] and f32 LSE with some -inf (empty) splits,

@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ["mla_kv_write", "mla_decode_partial", "mla_merge_lse", "mla_value_gate", "mla_split_plan",
-              "mla_status_string"]:
+    for n in ["mla_kv_write", "mla_decode_partial", "mla_decode_partial_fp8q", "mla_merge_lse",
+              "mla_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
 
@@ -86,7 +86,16 @@ def test_argument_errors_before_device_work(mlib):
                                 null, 0, 0, 0, null, 0, 0, 0, null) == 1
     assert L.mla_decode_partial(null, 576, 576, 2, 0, 16, null, 10, null, null, 0.1, 1.0, 2, 8, 1,
                                 null, 0, 0, 0, null, 0, 0, 0, null) == 1  # qlen 0
-    assert L.mla_merge_lse(null, 0, 0, 0, null, 0, 0, 0, 0, 4, 4, null, 0, 0, null, 0, 0, null) == 1
+    assert L.mla_decode_partial_fp8q(null, 576, 576, 0.5, 2, 1, 16, null, 10, null, null, 0.1, 1.0, 2, 8,
+                                     1, null, 0, 0, 0, null, 0, 0, 0, null) == 1
+    # (never dereferenced: every case below is rejected before a launch)
+    fake = ctypes.c_void_p(1 << 20)
+    args = lambda qs, sr: (fake, sr, 576, qs, 2, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2, 8, 1, fake, 0, 0, 0,
+                           fake, 0, 0, 0, null)
+    assert L.mla_decode_partial_fp8q(*args(0.0, 576)) == 1            # q_scale must be > 0
+    assert L.mla_decode_partial_fp8q(*args(float("nan"), 576)) == 1
+    assert L.mla_decode_partial_fp8q(*args(float("inf"), 576)) == 1
+    assert L.mla_decode_partial_fp8q(*args(0.5, 584)) == 2            # fp8 row stride not 16-B aligned
     assert L.mla_merge_lse(null, 0, 0, 0, null, 0, 0, 0, 2, 0, 4, null, 0, 0, null, 0, 0, null) == 0
     assert L.mla_value_gate(null, 0, 0, 0, null, 0, 0, null, 0, 0, null, 0, null, 6, 4, 2, null, 0,
                             null) == 1  # rows not a multiple of qlen

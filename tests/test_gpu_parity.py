@@ -118,15 +118,17 @@ def _run_step(ops, w, **kw):
     return st
 
 
-def _check_partials(oracle, w, st, cache):
+def _check_partials(oracle, w, st, cache, q8=None, q_scale=None):
+    """Partials against the oracle's; q8 / q_scale: the fp8 query the step ran on."""
     H = w.heads
     bounds, chunk = oracle.split_bounds(w.indptr, w.num_splits, st.num_workers, st.split_min)
     import mla_latent_kv_fp8_amd as m
 
     lib_bounds, lib_chunk = m.split_plan(w.indptr, w.num_splits, st.num_workers, st.split_min)
     assert lib_chunk == chunk and np.array_equal(lib_bounds, bounds)
-    q = np.ascontiguousarray(w.q[:, :H])
-    o_ref, l_ref = oracle.decode_partial(q, cache, w.indptr, w.indices, bounds, w.qlen, w.sm_scale, w.kv_scale)
+    q = np.ascontiguousarray((w.q if q8 is None else q8)[:, :H])
+    o_ref, l_ref = oracle.decode_partial(q, cache, w.indptr, w.indices, bounds, w.qlen, w.sm_scale, w.kv_scale,
+                                         q_scale=q_scale)
     lse = st.lse_part.cpu().numpy().astype(np.float64)
     o = oracle.bf16_decode(_np_bf16(st.o_part))
     fin = np.isfinite(l_ref)
@@ -189,6 +191,66 @@ def test_step_parity_small(ops, oracle, name, batch, lr, nw, smin):
     assert np.array_equal(st.kv_cache.cpu().numpy(), cache), "cache bytes differ"
     _check_partials(oracle, w, st, cache)
     _check_merge_and_value(oracle, w, st)
+
+
+# ------------------------------------------------------ fp8 query (q8)
+
+Q8_SMALL = [
+    # name, batch override, length range, num_workers, split_min, q_scale
+    ("tiny", None, None, None, None, 0.0625),
+    ("batch", 6, (100, 700), 8, 16, 0.03),
+    ("batch", 5, (1, 70), 16, 1, 0.0625),
+    ("spec_q4", 3, (60, 300), 4, 16, 0.07),
+    ("spec_q8", 2, (64, 200), 4, 8, 0.0625),
+    ("rank_share", 4, (100, 500), 8, 32, 0.05),
+]
+
+
+@pytest.mark.parametrize("name,batch,lr,nw,smin,q_scale", Q8_SMALL)
+def test_fp8_query_parity_small(ops, oracle, name, batch, lr, nw, smin, q_scale):
+    """mla_decode_partial_fp8q against the oracle on the same fp8 query
+    codes and scale (16-, 32- and 48-row workgroups, ragged tails)."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"fp8 query parity {name} batch={batch} lengths={lr} q_scale={q_scale}")
+    w = synth.make(name, batch=batch, len_range=lr)
+    q8, _ = synth.fp8_query(np.random.default_rng(300 + (batch or 0)), w.q.shape, w.heads)
+    st = DeviceStep(w, num_workers=nw, split_min_tokens=smin)
+    st.q, st.q_scale = torch.from_numpy(q8).cuda(), q_scale
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache, q8=q8, q_scale=q_scale)
+    _check_merge_and_value(oracle, w, st)
+
+
+@pytest.mark.parametrize("heads", [16, 32, 96])
+def test_fp8_query_power_of_two_scale_is_the_bf16_query(ops, heads, monkeypatch):
+    """With q_scale = 2^-4 every decoded query element q_scale * fp8(code) is
+    exactly a bf16 value, and every score of the two entry points differs by
+    an exact power of two that the score constant undoes: the fp8-query
+    partials must equal the bf16-query partials bit for bit."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"fp8 query == bf16 query bitwise ({heads} heads)")
+    spec = dict(synth.SPECS["batch"], heads=heads, heads_pad=128 if heads == 96 else heads)
+    monkeypatch.setitem(synth.SPECS, "batch", spec)
+    w = synth.make("batch", batch=4, len_range=(50, 900))
+    q8, _ = synth.fp8_query(np.random.default_rng(17), w.q.shape, w.heads)
+    real = torch.from_numpy(q8).view(torch.float8_e4m3fn).float() * 0.0625
+    a = DeviceStep(w, num_workers=16, split_min_tokens=16)
+    a.q, a.q_scale = torch.from_numpy(q8).cuda(), 0.0625
+    b = DeviceStep(w, num_workers=16, split_min_tokens=16)
+    b.q = real.to(torch.bfloat16).cuda()
+    assert torch.equal(b.q.float().cpu()[:, :heads], real[:, :heads])  # exactly representable
+    a.attend()
+    b.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(a.lse_part, b.lse_part)
+    fin = torch.isfinite(a.lse_part)
+    assert torch.equal(a.o_part.view(torch.int16)[fin], b.o_part.view(torch.int16)[fin])
 
 
 def test_end_to_end_chain_tiny(ops, oracle):
@@ -382,16 +444,22 @@ def test_single_split_and_one_token(ops, oracle):
 
 # ------------------------------------------- full size, sampled (bench launch)
 
-@pytest.mark.parametrize("name", ["batch", "long", "spec_q8", "rank_share"])
-def test_full_size_sampled(ops, oracle, name):
+@pytest.mark.parametrize("name,fp8_q", [("batch", False), ("long", False), ("spec_q8", False),
+                                         ("rank_share", False), ("batch", True)])
+def test_full_size_sampled(ops, oracle, name, fp8_q):
     """The bench configuration at full size; the oracle recomputes a few
-    sampled requests (their cache rows written by the oracle itself)."""
+    sampled requests (their cache rows written by the oracle itself).  With
+    fp8_q the step runs on an fp8 query with a per-tensor scale."""
     from mla_latent_kv_fp8_amd import synth
     from mla_latent_kv_fp8_amd.step import DeviceStep
 
-    _announce(f"full-size sampled {name}")
+    _announce(f"full-size sampled {name} fp8 query={fp8_q}")
     w = synth.make(name)
     st = DeviceStep(w)
+    q_all, q_scale = w.q, None
+    if fp8_q:
+        q_all, q_scale = synth.fp8_query(np.random.default_rng(78), w.q.shape, w.heads)
+        st.q, st.q_scale = torch.from_numpy(q_all).cuda(), q_scale
     st.run()
     torch.cuda.synchronize()
     rng = np.random.default_rng(77)
@@ -412,9 +480,9 @@ def test_full_size_sampled(ops, oracle, name):
     sub_ptr = np.concatenate([[0], np.cumsum([w.lengths[r] for r in sample])]).astype(np.int32)
     sub_idx = np.concatenate([w.indices[w.indptr[r]:w.indptr[r + 1]] for r in sample]).astype(np.int32)
     rows_t = np.concatenate([np.arange(r * w.qlen, (r + 1) * w.qlen) for r in sample])
-    q = np.ascontiguousarray(w.q[rows_t][:, :H])
+    q = np.ascontiguousarray(q_all[rows_t][:, :H])
     o_ref, l_ref = oracle.decode_partial(q, cache, sub_ptr, sub_idx, bounds[sample], w.qlen, w.sm_scale,
-                                         w.kv_scale)
+                                         w.kv_scale, q_scale=q_scale)
     lse = st.lse_part.cpu().numpy()[:, rows_t].astype(np.float64)
     o = oracle.bf16_decode(_np_bf16(st.o_part[:, torch.from_numpy(rows_t).cuda()]))
     fin = np.isfinite(l_ref)
@@ -423,7 +491,8 @@ def test_full_size_sampled(ops, oracle, name):
     assert o_err_ok(o[fin], oracle.bf16_decode(oracle.bf16_round(o_ref))[fin])
     # merged latent of the sampled rows against the oracle's unsplit attention
     one = np.stack([np.zeros(len(sample), np.int32), sub_ptr[1:] - sub_ptr[:-1]], 1).astype(np.int32)
-    o1, l1 = oracle.decode_partial(q, cache, sub_ptr, sub_idx, one, w.qlen, w.sm_scale, w.kv_scale)
+    o1, l1 = oracle.decode_partial(q, cache, sub_ptr, sub_idx, one, w.qlen, w.sm_scale, w.kv_scale,
+                                   q_scale=q_scale)
     lat = oracle.bf16_decode(_np_bf16(st.latent[torch.from_numpy(rows_t).cuda(), :H]))
     f1 = np.isfinite(l1[0])
     assert o_err_ok(lat[f1], o1[0][f1])
