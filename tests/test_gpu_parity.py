@@ -253,6 +253,35 @@ def test_fp8_query_power_of_two_scale_is_the_bf16_query(ops, heads, monkeypatch)
     assert torch.equal(a.o_part.view(torch.int16)[fin], b.o_part.view(torch.int16)[fin])
 
 
+@pytest.mark.parametrize("heads", [16, 96])
+def test_fp8_query_restart_on_late_spike(ops, oracle, heads, monkeypatch):
+    """fp8 query: a late token aligned with one head's query outgrows the
+    reference by far more than 2^64, so the piece restarts; the decoded
+    query (registers and, for the 48-row block, LDS) must survive the
+    restart.  Exact attention still holds."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"fp8 query restart on a late spike ({heads} heads)")
+    spec = dict(synth.SPECS["batch"], heads=heads, heads_pad=128 if heads == 96 else heads)
+    monkeypatch.setitem(synth.SPECS, "batch", spec)
+    w = synth.make("batch", batch=2, len_range=(3000, 3000))
+    q8, _ = synth.fp8_query(np.random.default_rng(23), w.q.shape, w.heads)
+    qd = oracle.fp8_decode(q8)
+    for r, tok, h in ((0, 2600, 5), (1, 1500, heads - 2)):
+        row = w.indptr[r] + tok
+        sign = np.where(qd[r, h] >= 0, 1.0, -1.0).astype(np.float32)
+        w.kv_rows[row] = synth.to_bf16_bits(448.0 * sign)
+    w.slot_mapping[:] = -1  # keep the spike rows (no new-token overwrite)
+    st = DeviceStep(w, num_workers=2, split_min_tokens=1)
+    st.q, st.q_scale = torch.from_numpy(q8).cuda(), 0.0625
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache, q8=q8, q_scale=0.0625)
+    _check_merge_and_value(oracle, w, st)
+
+
 def test_end_to_end_chain_tiny(ops, oracle):
     """The oracle's own chain (its partials -> its merge -> its value) against
     the GPU chain, from the same inputs."""
