@@ -7,10 +7,14 @@ merge_lse -> value_gate.  Default workload: the batch-decode configuration
 kv_scale 0.05, context lengths uniform in [1024, 8192], 4 empty requests,
 bf16 W_UV).
 
-Each timed step is preceded (outside its HIP events) by a 512 MiB write
-that evicts the KV cache from L2 and the Infinity Cache, so `value` is a
-cold-cache, HBM-served figure; warm back-to-back numbers are reported
-alongside.  Prints ONE JSON line.
+Each timed step is preceded (outside its HIP events) by a read of a separate
+512 MiB buffer, which evicts the KV cache and everything else the step
+touched from L2 and the 256 MB Infinity Cache, so `value` is a cold-cache,
+HBM-served figure.  The eviction reads rather than writes: a 512 MiB write
+would leave as many dirty lines in the caches, to be written back to HBM
+during the timed step (measured: it halves the rate of a plain gather of the
+same cache rows).  Warm back-to-back numbers are reported alongside.  Prints
+ONE JSON line.
 """
 from __future__ import annotations
 
@@ -38,10 +42,24 @@ def parse():
                          "(mla_decode_partial_fp8q) instead of the bf16 query")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--gather-probe", action="store_true",
+                    help="only time a plain read of the workload's cache rows (libmla_probe.so), cold, as "
+                         "the practical HBM ceiling of the partial kernel's gather pattern")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+class Evict:
+    """Evicts L2 and the Infinity Cache by reading a 512 MiB buffer that no
+    timed work touches; the caches are left clean (no pending write-backs)."""
+
+    def __init__(self, torch):
+        self.buf = torch.ones(128 << 20, dtype=torch.float32, device="cuda")  # 512 MiB
+
+    def __call__(self):
+        self.buf.sum()  # a float reduction reads the buffer as is (no cast, no temporary)
 
 
 def copy_probe():
@@ -56,6 +74,48 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+
+
+def gather_probe(config, steps):
+    """Cold-cache rate of a kernel that only reads the workload's cache rows
+    (in page-table order, and sorted), with the bench's own eviction."""
+    import ctypes
+
+    import torch
+
+    from mla_latent_kv_fp8_amd import synth
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    L = ctypes.CDLL(os.path.join(here, "mla_latent_kv_fp8_amd", "libmla_probe.so"))
+    L.mla_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_int32, ctypes.c_void_p]
+    L.mla_probe_gather.restype = ctypes.c_int
+    w = synth.make(config, draw_kv=False)
+    kv = torch.zeros((w.num_slots, 576), dtype=torch.uint8, device="cuda")
+    evict = Evict(torch)
+    grid = 4096
+    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+    res = {"probe": "plain gather of the workload's cache rows, cold", "workload": config,
+           "bytes": int(w.total_tokens) * 576}
+    for order in ("page_table", "sorted"):
+        idx = np.sort(w.indices) if order == "sorted" else w.indices
+        ids = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        ev = []
+        for _ in range(steps):
+            evict()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = L.mla_probe_gather(kv.data_ptr(), ids.data_ptr(), ids.numel(), out.data_ptr(), grid, s)
+            b.record()
+            if rc != 0:
+                raise RuntimeError("mla_probe_gather failed (%d)" % rc)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        res[order] = {"us": round(us, 2), "GB/s": round(res["bytes"] / us / 1e3, 1),
+                      "frac_of_8TBs": round(res["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)}
+    print(json.dumps(res))
 
 
 def algorithmic(w):
@@ -141,6 +201,9 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.gather_probe:
+        gather_probe(args.config, max(args.steps, 5))
+        return
     import torch
 
     import mla_latent_kv_fp8_amd as m
@@ -155,7 +218,7 @@ def main():
     if args.fp8_query:
         q8, q_scale = synth.fp8_query(np.random.default_rng(w.seed + 77), w.q.shape, w.heads)
         st.q, st.q_scale = torch.from_numpy(q8).to(st.dev), q_scale
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    evict = Evict(torch)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -168,7 +231,7 @@ def main():
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     for i in range(K):
-        flush.zero_()  # evict L2 / Infinity Cache (outside the step's events)
+        evict()  # L2 and Infinity Cache hold nothing of the step (outside its events)
         ev[i][0].record()
         st.write_new_tokens()
         st.attend()
@@ -192,7 +255,7 @@ def main():
     # the partial kernel alone (its own events), cold
     pk = []
     for _ in range(K):
-        flush.zero_()
+        evict()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         st.attend()

@@ -12,6 +12,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_fp8.so")
+# measurement probe (bench.py --gather-probe), a library of its own: not the path's C ABI
+PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
+PROBE_SRC = "probe_gather.hip"
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["kv_write.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -41,6 +44,12 @@ def build() -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SRC), "-o", tmp],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (PROBE_SRC, r.stderr))
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
