@@ -62,6 +62,8 @@ def lib():
         L.orc_e8m0_decode.restype = f64
         L.orc_kv_write.argtypes = [P, i64, P, i64, P, i32, P, f32]
         L.orc_kv_write.restype = None
+        L.orc_concat_quant_fp8.argtypes = [P, P, f32, i32, i32, P]
+        L.orc_concat_quant_fp8.restype = None
         L.orc_split_bounds.argtypes = [P, i32, i32, i32, i32, P]
         L.orc_split_bounds.restype = i64
         L.orc_decode_partial.argtypes = [P, i32, i32, i32, P, P, P, P, i32, f64, f64, P, P]
@@ -145,6 +147,18 @@ def kv_write(kv_c, k_pe, slot_mapping, kv_cache, kv_scale: float) -> np.ndarray:
     n = slots.shape[0]
     lib().orc_kv_write(_p(kv_c), D_LATENT, _p(k_pe), D_ROPE, _p(slots), n, _p(out),
                        ctypes.c_float(kv_scale))
+    return out
+
+
+def concat_quant_fp8(ql_nope, q_pe, q_scale: float) -> np.ndarray:
+    """fp8 query codes [rows, H, 576] u8 of E(cat(ql_nope, q_pe) / q_scale);
+    ql_nope [rows, H, 512] and q_pe [rows, H, 64] are bf16 bits (uint16)."""
+    ql = _c(ql_nope, np.uint16)
+    pe = _c(q_pe, np.uint16)
+    rows, heads = ql.shape[0], ql.shape[1]
+    assert ql.shape == (rows, heads, D_LATENT) and pe.shape == (rows, heads, D_ROPE)
+    out = np.empty((rows, heads, D_QK), dtype=np.uint8)
+    lib().orc_concat_quant_fp8(_p(ql), _p(pe), ctypes.c_float(q_scale), rows, heads, _p(out))
     return out
 
 

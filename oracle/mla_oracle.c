@@ -148,6 +148,28 @@ void orc_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_p
   }
 }
 
+/* ------------------------------------------------- query concat + quant */
+
+/* The fp8 query of [MLA] `pre` (_decode_concat_quant_fp8_op(ql_nope, q_pe,
+ * q_scale)): the absorbed query row of (t, h) is [ql_nope (512) | q_pe (64)],
+ * each value divided by q_scale in binary32 and encoded with E.  Readings
+ * taken: the op's inputs are the bf16 ql_nope and q_pe (the pages show the
+ * call, not the op), and its division and rounding are those of the cache
+ * write above.  ql_nope [rows][heads][512], q_pe [rows][heads][64] (bf16
+ * bits), q8 [rows][heads][576], all contiguous. */
+void orc_concat_quant_fp8(const uint16_t* ql_nope, const uint16_t* q_pe, float q_scale, int32_t rows,
+                          int32_t heads, uint8_t* q8) {
+  for (int64_t th = 0; th < (int64_t)rows * heads; ++th) {
+    for (int c = 0; c < ORC_D_QK; ++c) {
+      uint16_t h = c < ORC_D_LATENT ? ql_nope[th * ORC_D_LATENT + c]
+                                    : q_pe[th * ORC_D_ROPE + (c - ORC_D_LATENT)];
+      float x = (float)orc_bf16_decode(h);
+      float scaled = x / q_scale; /* binary32 division */
+      q8[th * ORC_D_QK + c] = orc_fp8_encode((double)scaled);
+    }
+  }
+}
+
 /* ---------------------------------------------------------- split bounds */
 
 static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -543,3 +543,48 @@ def test_gate_closed_forms_and_empty_rows(oracle):
     half = oracle.bf16_decode(oracle.bf16_round(acc[keep])) / 2   # exact halving
     assert np.array_equal(oracle.bf16_decode(out[keep]), half)
     assert (out[~keep] == 0).all()                                  # +0 bits
+
+
+# ------------------------------------------- query concat + fp8 quant (q8)
+
+def _bf16_bits(x):
+    return (np.ascontiguousarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_concat_quant_matches_torch_cast_in_range(oracle):
+    # in range, E is torch's float8_e4m3fn cast of the binary32 quotient
+    # (library routine); the layout is [ql_nope | q_pe] per (row, head)
+    rng = np.random.default_rng(31)
+    ql = _bf16_bits(rng.standard_normal((5, 3, 512)).astype(np.float32) * 2.0)
+    pe = _bf16_bits(rng.standard_normal((5, 3, 64)).astype(np.float32) * 2.0)
+    for q_scale in (0.0625, 0.03, 1.7):
+        got = oracle.concat_quant_fp8(ql, pe, q_scale)
+        x = torch.cat([_bf16(ql), _bf16(pe)], -1).to(torch.float32) / torch.tensor(q_scale, dtype=torch.float32)
+        assert float(x.abs().max()) < 448
+        want = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(got, want), q_scale
+
+
+def test_concat_quant_is_the_cache_write_of_the_same_row(oracle):
+    # the query row and a cache row of the same 576 values quantise alike
+    rng = np.random.default_rng(32)
+    ql = _bf16_bits(rng.standard_normal((4, 2, 512)).astype(np.float32) * 30.0)
+    pe = _bf16_bits(rng.standard_normal((4, 2, 64)).astype(np.float32) * 30.0)
+    got = oracle.concat_quant_fp8(ql, pe, 0.05)
+    cache = oracle.kv_write(ql.reshape(8, 512), pe.reshape(8, 64), np.arange(8, dtype=np.int64),
+                            np.zeros((8, 576), np.uint8), 0.05)
+    assert np.array_equal(got.reshape(8, 576), cache)
+
+
+def test_concat_quant_closed_forms(oracle):
+    # a power-of-two scale round-trips every finite code; beyond 448 the code
+    # saturates; NaN gives 0x7F; the rope part lands at columns 512..575
+    codes = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = oracle.fp8_decode(codes) * 0.25
+    ql = np.zeros((1, 1, 512), np.uint16)
+    ql[0, 0, :codes.size] = _bf16_bits(vals)
+    pe = _bf16_bits(np.array([1e6, -1e6, np.nan, 448.0 * 0.25 * 1.0625] + [0.0] * 60, np.float32))
+    got = oracle.concat_quant_fp8(ql, pe.reshape(1, 1, 64), 0.25)
+    assert np.array_equal(got[0, 0, :codes.size], codes)
+    assert list(got[0, 0, 512:516]) == [0x7E, 0xFE, 0x7F, 0x7E]
+    assert (got[0, 0, 516:] == 0).all()
