@@ -38,8 +38,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="batch")
     ap.add_argument("--fp8-query", action="store_true",
-                    help="run the partials on an fp8 E4M3 query with a per-tensor scale "
-                         "(mla_decode_partial_fp8q) instead of the bf16 query")
+                    help="the fp8-query path: each step quantises the bf16 query to fp8 E4M3 with a "
+                         "per-tensor scale (mla_concat_quant_fp8) and attends on it "
+                         "(mla_decode_partial_fp8q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--gather-probe", action="store_true",
@@ -216,8 +217,9 @@ def main():
           file=sys.stderr, flush=True)
     st = DeviceStep(w)
     if args.fp8_query:
-        q8, q_scale = synth.fp8_query(np.random.default_rng(w.seed + 77), w.q.shape, w.heads)
-        st.q, st.q_scale = torch.from_numpy(q8).to(st.dev), q_scale
+        # the runtime's fp8 path: each step quantises the bf16 query (q_scale
+        # 1/16 for the N(0,1) synthetic query), then attends on the fp8 codes
+        st.use_fp8_query(1.0 / 16.0)
     evict = Evict(torch)
     torch.cuda.synchronize()
 
@@ -234,6 +236,8 @@ def main():
         evict()  # L2 and Infinity Cache hold nothing of the step (outside its events)
         ev[i][0].record()
         st.write_new_tokens()
+        if args.fp8_query:
+            st.quantize_query()
         st.attend()
         ev[i][1].record()
         st.merge()

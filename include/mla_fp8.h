@@ -8,6 +8,7 @@
  * (classes `MlaValue`, `MlaGate`) describe it:
  *
  *   mla_kv_write        new tokens' [kv_c | k_pe] rows -> fp8 cache rows
+ *   mla_concat_quant_fp8  absorbed query [ql_nope | q_pe] -> fp8 query rows
  *   mla_decode_partial  absorbed queries attend over the paged fp8 cache:
  *                       split-KV partials o (bf16) and LSE (f32)
  *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
@@ -78,6 +79,27 @@ const char* mla_status_string(int status);
 int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                  int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n, uint8_t* kv_cache,
                  int64_t num_slots, float kv_scale, void* stream);
+
+/*
+ * The fp8 query ([MLA] `pre`: _decode_concat_quant_fp8_op(ql_nope, q_pe,
+ * q_scale), whose output `attend` decodes on).  For row t < rows, head
+ * h < heads, c < 576, with x = [ql_nope[t][h][0:512] | q_pe[t][h][0:64]] (bf16):
+ *   q8[t][h][c] = E(x_c / q_scale),
+ * the division a correctly rounded binary32 division and E the encoder of
+ * mla_kv_write (round to nearest even, saturate to +-448, NaN -> 0x7F).  The
+ * result is the q8 of mla_decode_partial_fp8q, with the same q_scale.
+ *   ql_nope [rows][heads][512] bf16, strides (ln_row, ln_head), multiples of 8
+ *   q_pe    [rows][heads][64] bf16, strides (pe_row, pe_head), multiples of 8
+ *           (e.g. the rope slice of a [rows][heads][192] projection output)
+ *           both 16-byte aligned
+ *   q8      [rows][heads][576] u8, strides (q8_row, q8_head), multiples of 8,
+ *           8-byte aligned (otherwise MLA_ERR_UNSUPPORTED)
+ *   q_scale > 0 and finite (otherwise MLA_ERR_INVALID)
+ * rows = 0 is a no-op.
+ */
+int mla_concat_quant_fp8(const uint16_t* ql_nope, int64_t ln_row, int64_t ln_head, const uint16_t* q_pe,
+                         int64_t pe_row, int64_t pe_head, float q_scale, int32_t rows, int32_t heads,
+                         uint8_t* q8, int64_t q8_row, int64_t q8_head, void* stream);
 
 /*
  * Split-KV partial attention ([MLA] `attend`, `m1c_inputs`: partials

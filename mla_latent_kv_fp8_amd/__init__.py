@@ -43,6 +43,7 @@ def lib() -> ctypes.CDLL:
         L.mla_kv_write.argtypes = [P, i64, P, i64, P, i32, P, i64, f32, P]
         L.mla_decode_partial.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32,
                                          i32, P, i64, i64, i64, P, i64, i64, i64, P]
+        L.mla_concat_quant_fp8.argtypes = [P, i64, i64, P, i64, i64, f32, i32, i32, P, i64, i64, P]
         L.mla_decode_partial_fp8q.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32, f32,
                                               i32, i32, i32, P, i64, i64, i64, P, i64, i64, i64, P]
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
@@ -50,8 +51,8 @@ def lib() -> ctypes.CDLL:
                                     i64, i64, P]
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
-        for name in ("mla_kv_write", "mla_decode_partial", "mla_decode_partial_fp8q", "mla_split_plan",
-                     "mla_merge_lse", "mla_value_gate"):
+        for name in ("mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
+                     "mla_split_plan", "mla_merge_lse", "mla_value_gate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -92,6 +93,21 @@ def kv_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
                             _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0], float(kv_scale),
                             _stream())
     _check(st, "mla_kv_write")
+
+
+def concat_quant_fp8(ql_nope: torch.Tensor, q_pe: torch.Tensor, q_scale: float, q8: torch.Tensor) -> None:
+    """fp8 query q8 [rows, H, 576] (uint8 or float8_e4m3fn) = E(cat(ql_nope, q_pe) / q_scale), with
+    ql_nope [rows, H, 512] and q_pe [rows, H, 64] bf16 (strided views allowed)."""
+    rows, heads = ql_nope.shape[0], ql_nope.shape[1]
+    if ql_nope.shape[-1] != D_LATENT or tuple(q_pe.shape) != (rows, heads, D_ROPE):
+        raise MlaError("ql_nope must be [rows, H, 512] and q_pe [rows, H, 64]")
+    if q8.shape[0] != rows or q8.shape[1] < heads or q8.shape[2] != D_QK:
+        raise MlaError("q8 must be [rows, >=H, 576]")
+    st = lib().mla_concat_quant_fp8(
+        _dev(ql_nope, "ql_nope", _BF16), ql_nope.stride(0), ql_nope.stride(1), _dev(q_pe, "q_pe", _BF16),
+        q_pe.stride(0), q_pe.stride(1), float(q_scale), rows, heads, _dev(q8, "q8", _U8), q8.stride(0),
+        q8.stride(1), _stream())
+    _check(st, "mla_concat_quant_fp8")
 
 
 def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,

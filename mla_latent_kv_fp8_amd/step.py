@@ -10,7 +10,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import D_LATENT, D_QK, D_V, decode_partial, kv_write, merge_lse, value_gate
+from . import D_LATENT, D_QK, D_V, concat_quant_fp8, decode_partial, kv_write, merge_lse, value_gate
 from .synth import FP8_NAN, Workload
 
 
@@ -29,6 +29,7 @@ class DeviceStep:
         S, H, VH = w.S, w.heads, w.value_heads
         self.q = _bf16_dev(w.q, dev)
         self.q_scale = None  # set, with an fp8 self.q, for the fp8-query entry point
+        self.q_bf16 = None   # set by use_fp8_query: the bf16 query each step quantises
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
         self.indices = torch.from_numpy(w.indices).to(dev)
@@ -54,7 +55,20 @@ class DeviceStep:
         self.w_fp4 = torch.from_numpy(w.w_fp4).to(dev) if w.w_fp4 is not None else None
         self.w_scale = torch.from_numpy(w.w_scale).to(dev) if w.w_scale is not None else None
 
-    # the four calls ---------------------------------------------------------
+    def use_fp8_query(self, q_scale: float):
+        """Run the fp8-query path: every step first quantises the bf16 query
+        (ql_nope = dims 0..511, q_pe = dims 512..575 of the real heads) into an
+        fp8 query buffer with mla_concat_quant_fp8, and attends on that."""
+        w = self.w
+        self.q_bf16 = self.q
+        self.q = torch.full((w.S, w.heads_pad, D_QK), 0x7F, dtype=torch.uint8, device=self.dev)
+        self.q_scale = float(q_scale)
+
+    def quantize_query(self):
+        H = self.w.heads
+        concat_quant_fp8(self.q_bf16[:, :H, :D_LATENT], self.q_bf16[:, :H, D_LATENT:], self.q_scale, self.q[:, :H])
+
+    # the calls of one step -----------------------------------------------------
     def write_new_tokens(self):
         nr = self.new_rows
         kv_write(nr[:, :D_LATENT], nr[:, D_LATENT:], self.slot_mapping, self.kv_cache, self.w.kv_scale)
@@ -76,6 +90,8 @@ class DeviceStep:
     def run(self, write_new: bool = True):
         if write_new:
             self.write_new_tokens()
+        if self.q_bf16 is not None:
+            self.quantize_query()
         self.attend()
         self.merge()
         self.value()

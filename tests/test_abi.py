@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ["mla_kv_write", "mla_decode_partial", "mla_decode_partial_fp8q", "mla_merge_lse",
-              "mla_value_gate", "mla_split_plan", "mla_status_string"]:
+    for n in ["mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
+              "mla_merge_lse", "mla_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
 
@@ -96,6 +96,12 @@ def test_argument_errors_before_device_work(mlib):
     assert L.mla_decode_partial_fp8q(*args(float("nan"), 576)) == 1
     assert L.mla_decode_partial_fp8q(*args(float("inf"), 576)) == 1
     assert L.mla_decode_partial_fp8q(*args(0.5, 584)) == 2            # fp8 row stride not 16-B aligned
+    cq = lambda qs, lr, rows: (fake, lr, 512, fake, 192 * 4, 192, qs, rows, 4, fake, 2304, 576, null)
+    assert L.mla_concat_quant_fp8(*cq(0.5, 2048, 0)) == 0            # rows = 0: no-op
+    assert L.mla_concat_quant_fp8(null, 2048, 512, null, 768, 192, 0.5, 2, 4, null, 2304, 576, null) == 1
+    assert L.mla_concat_quant_fp8(*cq(0.0, 2048, 2)) == 1            # q_scale must be > 0
+    assert L.mla_concat_quant_fp8(*cq(float("inf"), 2048, 2)) == 1
+    assert L.mla_concat_quant_fp8(*cq(0.5, 2044, 2)) == 2            # bf16 stride not 16-B aligned
     assert L.mla_merge_lse(null, 0, 0, 0, null, 0, 0, 0, 2, 0, 4, null, 0, 0, null, 0, 0, null) == 0
     assert L.mla_value_gate(null, 0, 0, 0, null, 0, 0, null, 0, 0, null, 0, null, 6, 4, 2, null, 0,
                             null) == 1  # rows not a multiple of qlen

@@ -282,6 +282,63 @@ def test_fp8_query_restart_on_late_spike(ops, oracle, heads, monkeypatch):
     _check_merge_and_value(oracle, w, st)
 
 
+@pytest.mark.parametrize("rows,heads", [(7, 5), (64, 12), (1, 96)])
+def test_concat_quant_bitexact(ops, oracle, rows, heads):
+    """mla_concat_quant_fp8 byte for byte against the oracle, on strided views
+    (ql_nope inside a padded buffer, q_pe the rope slice of a [rows, H, 192]
+    projection output, q8 with padded heads), with ties, saturation, NaN, -0
+    and subnormals among the values."""
+    from mla_latent_kv_fp8_amd.synth import to_bf16_bits
+
+    _announce(f"concat_quant rows={rows} heads={heads}")
+    rng = np.random.default_rng(rows * 7 + heads)
+    x = (rng.standard_normal((rows, heads, 576)) * 6).astype(np.float32)
+    mids = ((oracle.fp8_decode(np.arange(0, 0x7F, dtype=np.uint8))[:-1] +
+             oracle.fp8_decode(np.arange(1, 0x7F, dtype=np.uint8))) / 2 * 0.25).astype(np.float32)
+    flat = x.reshape(-1)
+    flat[:mids.size] = mids
+    flat[mids.size:2 * mids.size] = -mids
+    flat[2 * mids.size:2 * mids.size + 8] = [1e9, -1e9, np.nan, -0.0, 1e-6, 113.0, 116.0, 448 * 0.25 * 1.03]
+    bits = to_bf16_bits(x)
+    ql_buf = np.zeros((rows, heads + 1, 528), np.uint16)
+    ql_buf[:, :heads, :512] = bits[..., :512]
+    proj = np.zeros((rows, heads, 192), np.uint16)
+    proj[..., 128:] = bits[..., 512:]
+    ql_dev = _bf16_dev(ql_buf)[:, :heads, :512]
+    pe_dev = _bf16_dev(proj)[..., 128:]
+    q8 = torch.full((rows, heads + 2, 584), 0x7F, dtype=torch.uint8, device="cuda")
+    for q_scale in (0.25, 0.037):
+        ops.concat_quant_fp8(ql_dev, pe_dev, q_scale, q8[:, :heads, :576])
+        torch.cuda.synchronize()
+        want = oracle.concat_quant_fp8(bits[..., :512], bits[..., 512:], q_scale)
+        got = q8.cpu().numpy()
+        assert np.array_equal(got[:, :heads, :576], want), q_scale
+        assert (got[:, heads:] == 0x7F).all() and (got[:, :, 576:] == 0x7F).all()  # pads untouched
+
+
+def test_fp8_query_chain_from_bf16_query(ops, oracle):
+    """The fp8 query path of the runtime's pre/attend/post: the bf16 absorbed
+    query is quantised by mla_concat_quant_fp8, then attended by
+    mla_decode_partial_fp8q, merged and projected; every stage against the
+    oracle (its own concat + quant, its fp8-query partials)."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("fp8 query chain: concat_quant -> partial_fp8q -> merge -> value")
+    w = synth.make("batch", batch=5, len_range=(100, 900))
+    H, q_scale = w.heads, 0.0625
+    st = DeviceStep(w, num_workers=16, split_min_tokens=32)
+    st.use_fp8_query(q_scale)  # each step: ql_nope = dims 0..511, q_pe = 512..575 of the bf16 query
+    st.run()
+    torch.cuda.synchronize()
+    q8 = st.q
+    q8_ref = oracle.concat_quant_fp8(w.q[:, :H, :512], w.q[:, :H, 512:], q_scale)
+    assert np.array_equal(q8.cpu().numpy()[:, :H], q8_ref)
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache, q8=q8_ref, q_scale=q_scale)
+    _check_merge_and_value(oracle, w, st)
+
+
 def test_end_to_end_chain_tiny(ops, oracle):
     """The oracle's own chain (its partials -> its merge -> its value) against
     the GPU chain, from the same inputs."""
