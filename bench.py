@@ -41,6 +41,9 @@ def parse():
                     help="the fp8-query path: each step quantises the bf16 query to fp8 E4M3 with a "
                          "per-tensor scale (mla_concat_quant_fp8) and attends on it "
                          "(mla_decode_partial_fp8q)")
+    ap.add_argument("--post", choices=("fused", "separate"), default="separate",
+                    help="merge + W_UV + gate as mla_merge_lse then mla_value_gate (the faster, measured), "
+                         "or as one call (mla_merge_value_gate; needs value heads == attention heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--gather-probe", action="store_true",
@@ -220,6 +223,7 @@ def main():
         # the runtime's fp8 path: each step quantises the bf16 query (q_scale
         # 1/16 for the N(0,1) synthetic query), then attends on the fp8 codes
         st.use_fp8_query(1.0 / 16.0)
+    st.fused_post = args.post == "fused" and w.value_heads == w.heads
     evict = Evict(torch)
     torch.cuda.synchronize()
 
@@ -240,8 +244,11 @@ def main():
             st.quantize_query()
         st.attend()
         ev[i][1].record()
-        st.merge()
-        st.value()
+        if st.fused_post:
+            st.merge_value()
+        else:
+            st.merge()
+            st.value()
         ev[i][2].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
@@ -295,6 +302,7 @@ def main():
                                                                   ", fp8 E4M3 + per-tensor scale" if args.fp8_query
                                                                   else " bf16", w.total_tokens, w.kv_scale,
                                                                   w.num_splits, w.num_workers, w.w_format),
+                   "post": "merge+W_UV+gate fused" if st.fused_post else "merge, then W_UV+gate",
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),

@@ -14,6 +14,7 @@
  *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
+ *   mla_merge_value_gate  the merge, W_UV and gate in one call (no latent written)
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
@@ -220,6 +221,27 @@ int mla_value_gate(const uint16_t* latent, int64_t l_row, int64_t l_head, int32_
                    int64_t ws_head, int64_t ws_v, const uint16_t* gate, int64_t g_row,
                    const int32_t* lengths, int32_t rows, int32_t qlen, int32_t heads,
                    uint16_t* out, int64_t out_row, void* stream);
+
+/*
+ * mla_merge_lse followed by mla_value_gate in one call ([MLA] `post`; [VALUE]
+ * `MlaValue`, which loads its weight fragments before the latent is ready).
+ * For row t, head h: the latent row is the merge of the split partials,
+ * exactly the bf16 value mla_merge_lse writes, and
+ *   out[t][h*128 + v] = bf16( f32(bf16(sum_l latent[t][h][l] * W(h, v, l))) * sigmoid_f32(gate[t][h*128 + v]) )
+ * when lengths[t / qlen] > 0, +0 otherwise: the output of mla_value_gate on
+ * that latent, bit for bit.  The latent is not written.
+ *   o_part, lse_part, num_splits  as for mla_merge_lse (rows x heads)
+ *   w_format, w_uv, w_scale, gate, lengths, out  as for mla_value_gate (the
+ *            value heads are the attention heads)
+ *   lse      [rows][heads] f32 (strides l_row, l_head), the merged LSE; nullable
+ * rows must be a multiple of qlen; rows = 0 is a no-op.
+ */
+int mla_merge_value_gate(const uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                         const float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                         int32_t num_splits, int32_t w_format, const void* w_uv, int64_t w_head, int64_t w_v,
+                         const uint8_t* w_scale, int64_t ws_head, int64_t ws_v, const uint16_t* gate,
+                         int64_t g_row, const int32_t* lengths, int32_t rows, int32_t qlen, int32_t heads,
+                         uint16_t* out, int64_t out_row, float* lse, int64_t l_row, int64_t l_head, void* stream);
 
 #ifdef __cplusplus
 }

@@ -46,13 +46,15 @@ def lib() -> ctypes.CDLL:
         L.mla_concat_quant_fp8.argtypes = [P, i64, i64, P, i64, i64, f32, i32, i32, P, i64, i64, P]
         L.mla_decode_partial_fp8q.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32, f32,
                                               i32, i32, i32, P, i64, i64, i64, P, i64, i64, i64, P]
+        L.mla_merge_value_gate.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, P, i64, i64, P, i64,
+                                           i64, P, i64, P, i32, i32, i32, P, i64, P, i64, i64, P]
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
         L.mla_merge_lse.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, i32, P, i64, i64, P,
                                     i64, i64, P]
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-                     "mla_split_plan", "mla_merge_lse", "mla_value_gate"):
+                     "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -196,3 +198,34 @@ def value_gate(latent: torch.Tensor, gate: torch.Tensor, lengths: torch.Tensor, 
         _dev(lengths, "lengths", (torch.int32,)), rows, qlen, heads, _dev(out, "out", _BF16), out.stride(0),
         _stream())
     _check(st, "mla_value_gate")
+
+
+def _weights(heads, w_uv, w_fp4, w_scale):
+    if w_uv is not None:
+        if w_uv.shape[0] < heads or w_uv.shape[1] != D_V or w_uv.shape[2] != D_LATENT:
+            raise MlaError("w_uv must be [heads, 128, 512]")
+        return W_BF16, _dev(w_uv, "w_uv", _BF16), w_uv.stride(0), w_uv.stride(1), 0, 0, 0
+    if w_fp4.shape[0] < heads or w_fp4.shape[1] != D_V or w_fp4.shape[2] != D_LATENT // 2:
+        raise MlaError("w_fp4 must be [heads, 128, 256]")
+    return (W_MXFP4, _dev(w_fp4, "w_fp4", (torch.uint8,)), w_fp4.stride(0), w_fp4.stride(1),
+            _dev(w_scale, "w_scale", (torch.uint8,)), w_scale.stride(0), w_scale.stride(1))
+
+
+def merge_value_gate(o_part: torch.Tensor, lse_part: torch.Tensor, gate: torch.Tensor, lengths: torch.Tensor,
+                     out: torch.Tensor, *, qlen: int, w_uv: torch.Tensor | None = None,
+                     w_fp4: torch.Tensor | None = None, w_scale: torch.Tensor | None = None,
+                     lse: torch.Tensor | None = None) -> None:
+    """Merge of the partials (o_part [splits, rows, heads, 512], lse_part
+    [splits, rows, heads]) fused with W_UV + gate -> out [rows, heads*128]
+    bf16 (+ the merged lse [rows, heads] f32); the latent is not written."""
+    ns, rows, heads = lse_part.shape
+    fmt, wp, wh, wv, sp, sh, sv = _weights(heads, w_uv, w_fp4, w_scale)
+    lp = 0 if lse is None else _dev(lse, "lse", (torch.float32,))
+    st = lib().mla_merge_value_gate(
+        _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
+        _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1), lse_part.stride(2),
+        ns, fmt, ctypes.c_void_p(wp), wh, wv, ctypes.c_void_p(sp), sh, sv, _dev(gate, "gate", _BF16),
+        gate.stride(0), _dev(lengths, "lengths", (torch.int32,)), rows, qlen, heads, _dev(out, "out", _BF16),
+        out.stride(0), ctypes.c_void_p(lp), 0 if lse is None else lse.stride(0),
+        0 if lse is None else lse.stride(1), _stream())
+    _check(st, "mla_merge_value_gate")

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libmla_fp8.so")
 PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
 PROBE_SRC = "probe_gather.hip"
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["kv_write.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip"]
+SOURCES = ["kv_write.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip", "merge_value.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

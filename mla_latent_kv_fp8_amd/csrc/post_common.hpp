@@ -45,7 +45,9 @@ __device__ __forceinline__ float wave_reduce(float x, F op) {
 // are never read.
 // Up to 64 splits (the common case) each lane's LSE is loaded once, by
 // merge_lse_load, and kept in a register; beyond that merge_rows re-reads
-// the LSEs in every pass.
+// the LSEs in every pass.  ONE = true asserts at most 64 splits: that
+// variant has no loads before the latent rows', so a caller's loads issued
+// after merge_lse_load are not waited for until then.
 template <int R>
 __device__ __forceinline__ void merge_lse_load(const float* const* lp, int64_t ls_split, int num_splits, int lane,
                                                float (&l1)[R]) {
@@ -53,12 +55,12 @@ __device__ __forceinline__ void merge_lse_load(const float* const* lp, int64_t l
   for (int r = 0; r < R; ++r) l1[r] = num_splits <= 64 && lane < num_splits ? lp[r][lane * ls_split] : -INFINITY;
 }
 
-template <int R>
+template <int R, bool ONE = false>
 __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_t* const* base, int64_t ls_split,
                                            int64_t os_split, int num_splits, int lane, const float (&l1)[R],
                                            u32x4 (&out)[R], float (&total)[R]) {
   float m[R], s[R], acc[R][8];
-  const bool one_pass = num_splits <= 64;
+  const bool one_pass = ONE || num_splits <= 64;
 #pragma unroll
   for (int r = 0; r < R; ++r) m[r] = one_pass ? l1[r] : -INFINITY;
   if (!one_pass) {

@@ -10,7 +10,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import D_LATENT, D_QK, D_V, concat_quant_fp8, decode_partial, kv_write, merge_lse, value_gate
+from . import (D_LATENT, D_QK, D_V, concat_quant_fp8, decode_partial, kv_write, merge_lse, merge_value_gate,
+               value_gate)
 from .synth import FP8_NAN, Workload
 
 
@@ -30,6 +31,9 @@ class DeviceStep:
         self.q = _bf16_dev(w.q, dev)
         self.q_scale = None  # set, with an fp8 self.q, for the fp8-query entry point
         self.q_bf16 = None   # set by use_fp8_query: the bf16 query each step quantises
+        # run() merges and projects in one call (possible when the value heads
+        # are the attention heads); off: mla_merge_lse, then mla_value_gate
+        self.fused_post = False
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
         self.indices = torch.from_numpy(w.indices).to(dev)
@@ -87,11 +91,21 @@ class DeviceStep:
         value_gate(self.latent, self.gate, self.lengths, self.out, qlen=w.qlen, w_uv=self.w_uv,
                    w_fp4=self.w_fp4, w_scale=self.w_scale)
 
+    def merge_value(self):
+        """The merge, W_UV and gate in one call (the value heads must be the
+        attention heads); self.latent is not written."""
+        w = self.w
+        merge_value_gate(self.o_part, self.lse_part, self.gate, self.lengths, self.out, qlen=w.qlen, w_uv=self.w_uv,
+                         w_fp4=self.w_fp4, w_scale=self.w_scale, lse=self.lse)
+
     def run(self, write_new: bool = True):
         if write_new:
             self.write_new_tokens()
         if self.q_bf16 is not None:
             self.quantize_query()
         self.attend()
-        self.merge()
-        self.value()
+        if self.fused_post:
+            self.merge_value()
+        else:
+            self.merge()
+            self.value()

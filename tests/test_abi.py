@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ["mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-              "mla_merge_lse", "mla_value_gate", "mla_split_plan", "mla_status_string"]:
+              "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
 
@@ -107,6 +107,12 @@ def test_argument_errors_before_device_work(mlib):
                             null) == 1  # rows not a multiple of qlen
     assert L.mla_value_gate(null, 0, 0, 7, null, 0, 0, null, 0, 0, null, 0, null, 8, 4, 2, null, 0,
                             null) == 1
+    mv = lambda rows, qlen, fmt, op: (op, 0, 0, 0, fake, 0, 0, 0, 2, fmt, fake, 65536, 512, null, 0, 0, fake,
+                                      512, fake, rows, qlen, 4, fake, 512, null, 0, 0, null)
+    assert L.mla_merge_value_gate(*mv(0, 1, 0, fake)) == 0                 # rows = 0: no-op
+    assert L.mla_merge_value_gate(*mv(6, 4, 0, fake)) == 1                 # rows not a multiple of qlen
+    assert L.mla_merge_value_gate(*mv(8, 4, 7, fake)) == 1                 # unknown weight format
+    assert L.mla_merge_value_gate(*mv(8, 4, 0, null)) == 1                 # null partials
     indptr = np.array([0, 5, 3], dtype=np.int32)  # negative length
     bounds = np.zeros((2, 3), np.int32)
     assert L.mla_split_plan(indptr.ctypes.data_as(ctypes.c_void_p), 2, 2, 4, 1,

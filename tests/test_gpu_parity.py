@@ -433,6 +433,93 @@ def test_value_gate_parity(ops, oracle, fmt, rows, qlen, heads):
     assert np.all(np.isfinite(oracle.bf16_decode(half)))
 
 
+# ------------------------------------------- fused merge + value + gate
+
+@pytest.mark.parametrize("fmt,ns,rows,qlen,heads", [("bf16", 16, 64, 1, 96), ("bf16", 3, 13, 1, 5),
+                                                    ("mxfp4", 5, 40, 4, 12), ("bf16", 1, 20, 4, 3),
+                                                    ("mxfp4", 70, 9, 1, 9)])
+def test_merge_value_gate_equals_the_two_calls(ops, oracle, fmt, ns, rows, qlen, heads):
+    """mla_merge_value_gate bit for bit against mla_merge_lse followed by
+    mla_value_gate on the same partials (empty splits, fully empty rows,
+    empty requests with NaN gates, ragged row blocks, one split and more than
+    64), and the output against the oracle's merge + value + gate."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.synth import BF16_NAN, to_bf16_bits
+
+    _announce(f"merge_value_gate {fmt} splits={ns} rows={rows} qlen={qlen} heads={heads}")
+    rng = np.random.default_rng(ns * 13 + rows + heads)
+    o, l = synth.random_partials(rng, ns, rows, heads, p_empty=0.3)
+    l[:, 0, 0] = -np.inf  # a fully empty (row, head)
+    B = rows // qlen
+    lengths = rng.integers(1, 5, B).astype(np.int32)
+    lengths[0] = 0
+    empty = np.repeat(lengths == 0, qlen)
+    l[:, empty] = -np.inf  # an empty request has no live split
+    gate = to_bf16_bits(rng.standard_normal((rows, heads * 128)).astype(np.float32))
+    gate[empty] = BF16_NAN
+    o_dev = torch.zeros((ns, rows, heads + 1, 512), dtype=torch.bfloat16, device="cuda")
+    o_dev[:, :, :heads] = _bf16_dev(o)
+    o_dev = o_dev[:, :, :heads]
+    l_dev = torch.from_numpy(l).cuda()
+    g_dev, len_dev = _bf16_dev(gate), torch.from_numpy(lengths).cuda()
+    if fmt == "bf16":
+        wkw = dict(w_uv=_bf16_dev(to_bf16_bits(rng.standard_normal((heads, 128, 512)).astype(np.float32) * 0.044)))
+        okw = dict(w_bf16=ops_np(wkw["w_uv"]))
+    else:
+        w4 = rng.integers(0, 256, (heads, 128, 256), dtype=np.uint8)
+        ws = rng.integers(118, 125, (heads, 128, 16)).astype(np.uint8)
+        wkw = dict(w_fp4=torch.from_numpy(w4).cuda(), w_scale=torch.from_numpy(ws).cuda())
+        okw = dict(w_fp4=w4, w_scale=ws)
+    # the two calls
+    lat = torch.full((rows, heads, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse2 = torch.empty((rows, heads), dtype=torch.float32, device="cuda")
+    out2 = torch.full((rows, heads * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.merge_lse(o_dev, l_dev, lat, lse2)
+    ops.value_gate(lat, g_dev, len_dev, out2, qlen=qlen, **wkw)
+    # the fused call
+    lse1 = torch.full((rows, heads), 7.0, dtype=torch.float32, device="cuda")
+    out1 = torch.full((rows, heads * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.merge_value_gate(o_dev, l_dev, g_dev, len_dev, out1, qlen=qlen, lse=lse1, **wkw)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.isneginf(), lse2.isneginf())
+    fin = torch.isfinite(lse2)
+    assert torch.equal(lse1[fin], lse2[fin])
+    # against the oracle: its merge of the same partials, then its value + gate
+    mo, _ = oracle.merge_lse(np.where(np.isfinite(l)[..., None], o, 0), l)
+    _, ref = oracle.value_gate(oracle.bf16_round(mo), gate, lengths, qlen, **okw)
+    got, want = oracle.bf16_decode(_np_bf16(out1)), oracle.bf16_decode(ref)
+    assert (_np_bf16(out1)[empty] == 0).all()
+    assert np.abs(got - want).max() <= OUT_REL_TOL * np.abs(want).max()
+
+
+def ops_np(t):
+    return _np_bf16(t)
+
+
+@pytest.mark.parametrize("name,batch,lr,nw,smin", [("batch", 6, (100, 700), 8, 16), ("spec_q4", 3, (60, 300), 4, 16)])
+def test_step_with_fused_post(ops, oracle, name, batch, lr, nw, smin):
+    """The whole step with the fused merge + value + gate: outputs against
+    the oracle, and bit for bit against the step with the two calls."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"step with fused post {name} batch={batch} lengths={lr}")
+    w = synth.make(name, batch=batch, len_range=lr)
+    a = DeviceStep(w, num_workers=nw, split_min_tokens=smin)
+    a.run()
+    b = DeviceStep(w, num_workers=nw, split_min_tokens=smin)
+    b.fused_post = True
+    b.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.lse, b.lse)
+    lat = _np_bf16(a.latent)
+    _, out_ref = oracle.value_gate(lat, w.gate, w.lengths, w.qlen, w_bf16=w.w_uv)
+    ref, got = oracle.bf16_decode(out_ref), oracle.bf16_decode(_np_bf16(b.out))
+    assert np.abs(got - ref).max() <= OUT_REL_TOL * np.abs(ref).max()
+
+
 # ------------------------------------------------------- invariants / edges
 
 def test_page_table_permutation_bitwise(ops):
