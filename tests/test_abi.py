@@ -117,3 +117,15 @@ def test_argument_errors_before_device_work(mlib):
     bounds = np.zeros((2, 3), np.int32)
     assert L.mla_split_plan(indptr.ctypes.data_as(ctypes.c_void_p), 2, 2, 4, 1,
                             bounds.ctypes.data_as(ctypes.c_void_p), null) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the bench measures one GPU; asking for more exits with a message and
+    # status 2 before anything touches a device
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
