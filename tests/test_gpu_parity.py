@@ -617,12 +617,14 @@ def test_single_split_and_one_token(ops, oracle):
 
 # ------------------------------------------- full size, sampled (bench launch)
 
-@pytest.mark.parametrize("name,fp8_q", [("batch", False), ("long", False), ("spec_q8", False),
-                                         ("rank_share", False), ("batch", True)])
+@pytest.mark.parametrize("name,fp8_q", [("batch", None), ("long", None), ("spec_q8", None),
+                                         ("rank_share", None), ("batch", "codes"), ("batch", "quantised")])
 def test_full_size_sampled(ops, oracle, name, fp8_q):
     """The bench configuration at full size; the oracle recomputes a few
     sampled requests (their cache rows written by the oracle itself).  With
-    fp8_q the step runs on an fp8 query with a per-tensor scale."""
+    fp8_q the step runs on an fp8 query with a per-tensor scale: drawn codes,
+    or the bf16 query quantised each step by mla_concat_quant_fp8 (the
+    bench's --fp8-query step)."""
     from mla_latent_kv_fp8_amd import synth
     from mla_latent_kv_fp8_amd.step import DeviceStep
 
@@ -630,10 +632,18 @@ def test_full_size_sampled(ops, oracle, name, fp8_q):
     w = synth.make(name)
     st = DeviceStep(w)
     q_all, q_scale = w.q, None
-    if fp8_q:
+    if fp8_q == "codes":
         q_all, q_scale = synth.fp8_query(np.random.default_rng(78), w.q.shape, w.heads)
         st.q, st.q_scale = torch.from_numpy(q_all).cuda(), q_scale
+    elif fp8_q == "quantised":
+        q_scale = 1.0 / 16.0
+        st.use_fp8_query(q_scale)
+        q_all = np.full(w.q.shape, 0x7F, np.uint8)
+        q_all[:, :w.heads] = oracle.concat_quant_fp8(w.q[:, :w.heads, :512], w.q[:, :w.heads, 512:], q_scale)
     st.run()
+    if fp8_q == "quantised":
+        torch.cuda.synchronize()
+        assert np.array_equal(st.q.cpu().numpy()[:, :w.heads], q_all[:, :w.heads])
     torch.cuda.synchronize()
     rng = np.random.default_rng(77)
     nonempty = np.flatnonzero(w.lengths > 0)
