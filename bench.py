@@ -280,6 +280,20 @@ def main():
     value = kv_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (partial_ms * 1e-3) / 1e12
     gbs_partial = kv_bytes / (partial_ms * 1e-3) / 1e9
+    # the partial kernel's bound: MFMA when its flops per KV byte exceed the
+    # chip's balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), else HBM
+    traffic = None if args.fp8_query else measured_traffic(args.config)
+    common = {"traffic": traffic, "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
+              "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+              "flop_per_byte": round(flops / max(kv_bytes, 1), 1)}
+    mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+    hbm_roof = {"bound": "hbm", "achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs_partial / HBM_PEAK_GBS, 4)}
+    if flops / max(kv_bytes, 1) > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof, other_key, other = dict(mfma_roof, **common), "roofline_hbm", hbm_roof
+    else:
+        roof, other_key, other = dict(hbm_roof, **common), "roofline_mfma", mfma_roof
     out = {
         "metric": "MLA decode: fp8-KV GB/s + MFMA TFLOP/s vs peak; us/step at B=64, H=128",
         "value": round(value, 2),
@@ -304,13 +318,9 @@ def main():
                                                                   w.num_splits, w.num_workers, w.w_format),
                    "post": "merge+W_UV+gate fused" if st.fused_post else "merge, then W_UV+gate",
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": None if args.fp8_query else measured_traffic(args.config),
-                     "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
-                     "flops_per_launch": flops},
-        "roofline_hbm": {"achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs_partial / HBM_PEAK_GBS, 4), "kv_bytes_per_launch": kv_bytes},
+        "roofline": roof,
+        # the other roof of the same kernel, for reference
+        other_key: other,
         "attend_us_in_step": round(float(np.mean(attn_ms)) * 1e3, 2),
         "wall_s_timed_region": round(t_wall, 3),
     }
