@@ -339,6 +339,31 @@ def test_fp8_query_chain_from_bf16_query(ops, oracle):
     _check_merge_and_value(oracle, w, st)
 
 
+@pytest.mark.parametrize("heads,qlen,fp8_q", [(7, 3, False), (40, 1, False), (5, 4, True), (40, 1, True)])
+def test_rows_not_a_multiple_of_16(ops, oracle, heads, qlen, fp8_q, monkeypatch):
+    """qlen * heads rows per request that leave a row group partly empty
+    (21, 40, 20 rows: the 32-, 48- and 32-row blocks compute rows past the
+    end on a copy of a real row and never store them), with bf16 and fp8
+    queries; partials, merge and value against the oracle."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"rows not a multiple of 16: heads={heads} qlen={qlen} fp8 query={fp8_q}")
+    spec = dict(synth.SPECS["spec_q4"], heads=heads, heads_pad=heads + 3, qlen=qlen, value_heads=heads)
+    monkeypatch.setitem(synth.SPECS, "spec_q4", spec)
+    w = synth.make("spec_q4", batch=3, len_range=(70, 400))
+    st = DeviceStep(w, num_workers=6, split_min_tokens=16)
+    q8, q_scale = None, None
+    if fp8_q:
+        q8, q_scale = synth.fp8_query(np.random.default_rng(heads), w.q.shape, w.heads)
+        st.q, st.q_scale = torch.from_numpy(q8).cuda(), q_scale
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache, q8=q8, q_scale=q_scale)
+    _check_merge_and_value(oracle, w, st)
+
+
 def test_end_to_end_chain_tiny(ops, oracle):
     """The oracle's own chain (its partials -> its merge -> its value) against
     the GPU chain, from the same inputs."""
