@@ -1,9 +1,15 @@
 """One decode step of the path on device buffers: kv_write -> decode_partial
 -> merge_lse -> value_gate, for a synthetic workload (see synth.py).
 
+Two variants of the same step: `use_fp8_query(q_scale)` quantises the bf16
+query with concat_quant_fp8 each step and attends on the fp8 codes
+(decode_partial with q_scale); `fused_post = True` runs merge_value_gate in
+place of merge_lse + value_gate (the value heads must be the attention
+heads).
+
 Buffers are allocated once by `DeviceStep.__init__` (torch, on the current
-device) and reused by every `run()`, so a timed step enqueues the four
-library calls and nothing else.
+device) and reused by every `run()`, so a timed step enqueues the library
+calls and nothing else.
 """
 from __future__ import annotations
 
@@ -95,6 +101,9 @@ class DeviceStep:
         """The merge, W_UV and gate in one call (the value heads must be the
         attention heads); self.latent is not written."""
         w = self.w
+        if w.value_heads != w.heads:
+            raise ValueError("merge_value needs the value heads (%d) to be the attention heads (%d)"
+                             % (w.value_heads, w.heads))
         merge_value_gate(self.o_part, self.lse_part, self.gate, self.lengths, self.out, qlen=w.qlen, w_uv=self.w_uv,
                          w_fp4=self.w_fp4, w_scale=self.w_scale, lse=self.lse)
 
