@@ -364,6 +364,37 @@ def test_rows_not_a_multiple_of_16(ops, oracle, heads, qlen, fp8_q, monkeypatch)
     _check_merge_and_value(oracle, w, st)
 
 
+def test_requests_shorter_than_the_window(ops, oracle):
+    """qlen 4 with requests of 1, 2, 3, 0 and 6 tokens: row j of a window
+    sees max(0, L - qlen + j + 1) tokens, so the first rows of the short
+    requests see none (LSE -inf in every split, latent zero), the others a
+    prefix.  Partials, merge and value against the oracle."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce("requests shorter than the speculative window (qlen 4)")
+    w = synth.make("spec_q4", batch=5, len_range=(8, 12))
+    new_len = np.array([1, 2, 3, 0, 6], dtype=np.int64)
+    keep = np.concatenate([np.arange(w.indptr[r], w.indptr[r] + new_len[r]) for r in range(w.batch)])
+    w.kv_rows = w.kv_rows[keep]
+    w.indices = w.indices[keep]
+    w.lengths = new_len.astype(np.int32)
+    w.indptr = np.concatenate([[0], np.cumsum(new_len)]).astype(np.int32)
+    w.slot_mapping[:] = -1  # the cache already holds every row
+    st = DeviceStep(w, num_workers=3, split_min_tokens=1)
+    st.run()
+    torch.cuda.synchronize()
+    cache = _oracle_cache(oracle, w)
+    _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
+    lat = oracle.bf16_decode(_np_bf16(st.latent[:, :w.heads]))
+    for r in range(w.batch):
+        for j in range(w.qlen):
+            t = r * w.qlen + j
+            if new_len[r] - w.qlen + j + 1 <= 0:
+                assert (lat[t] == 0).all() and torch.isneginf(st.lse[t]).all(), (r, j)
+
+
 def test_end_to_end_chain_tiny(ops, oracle):
     """The oracle's own chain (its partials -> its merge -> its value) against
     the GPU chain, from the same inputs."""
