@@ -199,7 +199,7 @@ def cpu_baseline(w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+        print("bench.py measures one GPU only: the library has no multi-GPU path (--gpus %d refused)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
