@@ -133,6 +133,36 @@ def algorithmic(w):
     return kv_bytes, flops
 
 
+def step_bytes(w, num_workers, split_min):
+    """Algorithmic bytes of one whole step, by tensor: each byte a kernel must
+    read or write once.  Live partial entries (splits that hold tokens for a
+    row) come from the library's host-side split plan."""
+    import mla_latent_kv_fp8_amd as m
+
+    S, H, VH = w.S, w.heads, w.value_heads
+    bounds, _ = m.split_plan(w.indptr, w.num_splits, num_workers, split_min)
+    live = 0
+    for r in range(w.batch):
+        L = int(w.lengths[r])
+        for j in range(w.qlen):
+            vis = max(0, L - w.qlen + j + 1)
+            b = np.minimum(bounds[r], vis)
+            live += int((np.diff(b) > 0).sum())
+    n_new = int((w.slot_mapping >= 0).sum())
+    w_bytes = VH * 128 * 512 * 2 if w.w_format == "bf16" else VH * 128 * (256 + 16)
+    parts = {
+        "kv_write": n_new * (2 * 576 + 8 + 576),
+        "query": S * H * 576 * 2,
+        "kv_cache": int(w.total_tokens) * (576 + 4),
+        "partials": 2 * live * H * (512 * 2 + 4),  # written by the partial kernel, read by the merge
+        "latent": 2 * S * H * 512 * 2,             # written by the merge, read by W_UV
+        "w_uv": w_bytes,
+        "gate_and_out": 2 * S * VH * 128 * 2,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
 def measured_traffic(config):
     """HBM bytes per launch of the partial kernel from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-probe calibration),
@@ -280,6 +310,7 @@ def main():
     value = kv_bytes / (ms * 1e-3) / 1e9
     tflops = flops / (partial_ms * 1e-3) / 1e12
     gbs_partial = kv_bytes / (partial_ms * 1e-3) / 1e9
+    sb = step_bytes(w, st.num_workers, st.split_min)
     # the partial kernel's bound: MFMA when its flops per KV byte exceed the
     # chip's balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), else HBM
     traffic = None if args.fp8_query else measured_traffic(args.config)
@@ -321,6 +352,8 @@ def main():
         "roofline": roof,
         # the other roof of the same kernel, for reference
         other_key: other,
+        "step_bytes": sb,
+        "step_gbs_all_bytes": round(sb["total"] / (ms * 1e-3) / 1e9, 1),
         "attend_us_in_step": round(float(np.mean(attn_ms)) * 1e3, 2),
         "wall_s_timed_region": round(t_wall, 3),
     }

@@ -129,3 +129,20 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_bench_step_bytes_counts_live_splits():
+    # the whole-step byte count: one partial entry per (row, split) that holds
+    # tokens for the row, no more than num_splits per row, and at least one
+    # for every row that sees a token
+    import bench
+    from mla_latent_kv_fp8_amd import synth
+
+    w = synth.make("rank_share", seed=5, batch=6, draw_kv=False)
+    sb = bench.step_bytes(w, w.num_workers, w.split_min_tokens)
+    assert w.num_splits > 1
+    live = sb["partials"] // (2 * w.heads * (512 * 2 + 4))
+    seen = sum(1 for r in range(w.batch) for j in range(w.qlen) if int(w.lengths[r]) - w.qlen + j + 1 > 0)
+    assert seen <= live <= w.num_splits * w.S
+    assert sb["kv_cache"] == int(w.total_tokens) * 580
+    assert sb["total"] == sum(v for k, v in sb.items() if k != "total")
