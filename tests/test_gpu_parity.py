@@ -364,6 +364,34 @@ def test_rows_not_a_multiple_of_16(ops, oracle, heads, qlen, fp8_q, monkeypatch)
     _check_merge_and_value(oracle, w, st)
 
 
+@pytest.mark.parametrize("case", ["heads_128", "splits_1024"])
+def test_maximum_sizes(ops, oracle, case, monkeypatch):
+    """The largest padded head count (128 heads, no pad: row blocks of 48, 48
+    and 32) and the largest split count (1024 splits of about four tokens,
+    750 and 1000 of them live, so the merge takes its multi-pass path);
+    partials, merge and value against the oracle."""
+    from mla_latent_kv_fp8_amd import synth
+
+    _announce(f"maximum sizes: {case}")
+    if case == "heads_128":
+        spec = dict(synth.SPECS["batch"], heads=128, heads_pad=128, value_heads=128, empty=1)
+        monkeypatch.setitem(synth.SPECS, "batch", spec)
+        w = synth.make("batch", batch=3, len_range=(100, 700))
+        st = _run_step(ops, w, num_workers=8, split_min_tokens=16)
+    else:
+        spec = dict(synth.SPECS["batch"], batch=2, heads=16, heads_pad=16, value_heads=16, num_splits=1024,
+                    fixed_lengths=[3000, 4000], empty=0)
+        monkeypatch.setitem(synth.SPECS, "batch", spec)
+        w = synth.make("batch")
+        st = _run_step(ops, w, num_workers=4096, split_min_tokens=1)
+        live = (st.lse_part.cpu().numpy() > -np.inf).sum(axis=0)
+        assert live.min() == 750 and live.max() == 1000
+    cache = _oracle_cache(oracle, w)
+    assert np.array_equal(st.kv_cache.cpu().numpy(), cache), "cache bytes differ"
+    _check_partials(oracle, w, st, cache)
+    _check_merge_and_value(oracle, w, st)
+
+
 def test_requests_shorter_than_the_window(ops, oracle):
     """qlen 4 with requests of 1, 2, 3, 0 and 6 tokens: row j of a window
     sees max(0, L - qlen + j + 1) tokens, so the first rows of the short
