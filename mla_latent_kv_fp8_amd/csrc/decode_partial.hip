@@ -147,6 +147,12 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots,
 
 constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
 constexpr int NBUF = 3;        // staged tiles in flight (triple buffering)
+// K-steps by which QK reads the query's LDS part ahead of its MFMAs: with one
+// wave per SIMD the LDS returns data only as fast as reads are in flight, and
+// two steps of reads (24 more VGPRs than one) keep more of them in flight
+#ifndef MLA_QLDS_AHEAD
+#define MLA_QLDS_AHEAD 2
+#endif
 #ifndef QREG3
 #define QREG3 5
 #endif
@@ -415,9 +421,9 @@ __device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_
 // S[g] (16 tokens x 16 rows, C layout: tokens 4*(l/16).. of row l%16) =
 // K . Q^T over the 576 dims, as 9 K-step pairs.  Step pp uses chunk 4pp+lg
 // of token 16*wave+lr (block (wave, pp) of the staged tile); K reads run
-// two steps ahead of their conversion, LDS-resident query fragments one
-// step ahead of their MFMAs, and each step interleaves its MFMAs with the
-// conversions of the next step.
+// two steps ahead of their conversion, LDS-resident query fragments
+// MLA_QLDS_AHEAD steps ahead of their MFMAs, and each step interleaves its
+// MFMAs with the conversions of the next step.
 template <int NRG, int QR>
 __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 (&qf)[NRG][2 * QR],
                                         const MLA_LDS uint8_t* qlds, int wave, int lane, f32x4 (&S)[NRG]) {
@@ -429,24 +435,31 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
   u32x4 raw[3];
   raw[0] = *(const MLA_LDS u32x4*)kq;
   raw[1] = *(const MLA_LDS u32x4*)(kq + 1024);
-  bf16x8 ql[2][NRG][2];
-  if (QR == 0) {
+  // LDS-resident query fragments are read QLA K-steps ahead of their MFMAs
+  constexpr int QLA = MLA_QLDS_AHEAD;
+  bf16x8 ql[QLA + 1][NRG][2];
 #pragma unroll
-    for (int g = 0; g < NRG; ++g)
+  for (int s0 = 0; s0 < QLA; ++s0) {
+    if (s0 >= QR && s0 < 9) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) ql[0][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 64 * h);
+      for (int g = 0; g < NRG; ++g)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ql[s0 % (QLA + 1)][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * s0 + 64 * h);
+    }
   }
   bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
   bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
 #pragma unroll
   for (int pp = 0; pp < 9; ++pp) {
     if (pp + 2 < 9) raw[(pp + 2) % 3] = *(const MLA_LDS u32x4*)(kq + 1024 * (pp + 2));
-    if (pp + 1 >= QR && pp + 1 < 9) {
+    if (pp + QLA >= QR && pp + QLA < 9) {
 #pragma unroll
       for (int g = 0; g < NRG; ++g)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          ql[(pp + 1) & 1][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + 1) + 64 * h);
+          ql[(pp + QLA) % (QLA + 1)][g][h] =
+              *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + QLA) + 64 * h);
     }
     bf16x8 nlo = klo, nhi = khi;
     if (pp + 1 < 9) {
@@ -459,8 +472,8 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
         S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
         S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
       } else {
-        S[g] = mfma16(klo, ql[pp & 1][g][0], S[g]);
-        S[g] = mfma16(khi, ql[pp & 1][g][1], S[g]);
+        S[g] = mfma16(klo, ql[pp % (QLA + 1)][g][0], S[g]);
+        S[g] = mfma16(khi, ql[pp % (QLA + 1)][g][1], S[g]);
       }
     }
     klo = nlo;
