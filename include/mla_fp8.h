@@ -76,6 +76,9 @@ const char* mla_status_string(int status);
  *   slot_mapping [n] int64
  *   kv_cache     [num_slots][576] u8, rows contiguous
  * n = 0 is a no-op.
+ * Errors: MLA_ERR_INVALID for n < 0, num_slots < 0, a null pointer,
+ * kv_c_stride < 512, k_pe_stride < 64, or kv_scale not positive and finite;
+ * MLA_ERR_UNSUPPORTED when n * 72 threads exceed one launch grid.
  */
 int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                  int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n, uint8_t* kv_cache,
@@ -136,7 +139,13 @@ int mla_concat_quant_fp8(const uint16_t* ql_nope, int64_t ln_row, int64_t ln_hea
  * q: [S][...][576] bf16 with strides (q_stride_row, q_stride_head); the
  * query buffer may carry padded heads beyond `heads` (never read).
  * kv_cache: [num_slots][576] u8.  Requires 1 <= num_splits <= 1024,
- * num_workers >= 1, qlen >= 1, heads >= 1.
+ * num_workers >= 1, qlen >= 1, heads >= 1.  batch = 0 is a no-op.
+ * Errors: MLA_ERR_INVALID for a size outside those ranges, batch < 0, a null
+ * pointer, num_slots outside [1, 2^31 - 1], or sm_scale or kv_scale not
+ * positive; MLA_ERR_UNSUPPORTED unless q is 16-byte aligned with strides
+ * that are multiples of 8, o_part is 8-byte aligned with strides that are
+ * multiples of 4 and kv_cache is 16-byte aligned, or when qlen * heads
+ * exceeds 2^20 or the grid (num_workers x row blocks) exceeds one launch.
  */
 int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
                        int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
@@ -192,6 +201,10 @@ int mla_split_plan(const int32_t* kv_indptr_host, int32_t batch, int32_t num_spl
  *   o        [rows][heads][512] bf16 (strides o_row, o_head)
  *   lse      [rows][heads] f32 (strides l_row, l_head), nullable
  * rows = 0 is a no-op.
+ * Errors: MLA_ERR_INVALID for rows < 0, heads < 1, num_splits < 1 or a null
+ * pointer (lse aside); MLA_ERR_UNSUPPORTED unless os_split, os_row, os_head,
+ * o_row and o_head are multiples of 8 and o_part and o are 16-byte aligned,
+ * or when rows * heads exceeds one launch grid.
  */
 int mla_merge_lse(const uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                   const float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
@@ -215,6 +228,14 @@ int mla_merge_lse(const uint16_t* o_part, int64_t os_split, int64_t os_row, int6
  *   lengths [rows / qlen] int32
  *   out    [rows][heads*128] bf16 (stride out_row)
  * rows must be a multiple of qlen; rows = 0 is a no-op.
+ * Errors: MLA_ERR_INVALID for rows < 0, qlen < 1, heads < 1, rows not a
+ * multiple of qlen, a null pointer (w_scale is needed for MXFP4 only),
+ * g_row or out_row < heads*128, W strides smaller than one [128][512]
+ * head, or an unknown w_format; MLA_ERR_UNSUPPORTED unless l_row and l_head
+ * are multiples of 8 with latent 16-byte aligned, g_row and out_row are
+ * multiples of 4 with gate and out 8-byte aligned, and the W strides are
+ * multiples of 8 with w_uv 16-byte aligned (bf16) or multiples of 4 with
+ * w_uv 4-byte aligned (MXFP4).
  */
 int mla_value_gate(const uint16_t* latent, int64_t l_row, int64_t l_head, int32_t w_format,
                    const void* w_uv, int64_t w_head, int64_t w_v, const uint8_t* w_scale,
@@ -235,6 +256,10 @@ int mla_value_gate(const uint16_t* latent, int64_t l_row, int64_t l_head, int32_
  *            value heads are the attention heads)
  *   lse      [rows][heads] f32 (strides l_row, l_head), the merged LSE; nullable
  * rows must be a multiple of qlen; rows = 0 is a no-op.
+ * Errors: those of mla_value_gate for the weights, gate, lengths and out;
+ * also MLA_ERR_INVALID for num_splits < 1 or a null o_part or lse_part, and
+ * MLA_ERR_UNSUPPORTED unless os_split, os_row and os_head are multiples of
+ * 8 and o_part is 16-byte aligned, or when the grid exceeds one launch.
  */
 int mla_merge_value_gate(const uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                          const float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
