@@ -62,6 +62,24 @@ struct PartialArgs {
   int64_t ls_s, ls_r, ls_h;
 };
 
+// The split partition computed on the host (the one the kernel derives from
+// kv_indptr, unit by unit), passed in the kernel arguments: a workgroup then
+// starts its first piece without first reading the request offsets and
+// searching them.
+constexpr int PLAN_UNITS = 192;  // units one plan holds (the arguments stay under 4 KB)
+constexpr int PLAN_RP = 128;     // request offsets of a unit staged in LDS (2 waves x 64)
+template <bool PLAN>
+struct UnitPlan {};
+template <>
+struct UnitPlan<true> {
+  int64_t chunk, nunits, Tv;
+  int32_t base, pad_;
+  int32_t r[PLAN_UNITS];      // first request of unit u
+  int32_t r_end[PLAN_UNITS];  // one past its last request
+  int32_t p0[PLAN_UNITS];     // kv_indptr[r] - kv_indptr[0]
+  int32_t len0[PLAN_UNITS];   // L_r
+};
+
 // LDS layout of a staged tile (64 tokens x 36 chunks of 16 B): block
 // (t/16, c/4) of 1 KB holds 16 tokens x 4 chunks; inside it, chunk c of
 // token t sits at 16-B slot 4*(t%16) + ((c%4) ^ h(t)).  This h makes both
@@ -535,8 +553,8 @@ __device__ __forceinline__ void decode_q8(const MLA_LDS uint8_t* q8s, MLA_LDS ui
   }
 }
 
-template <int NRG, bool QF8>
-__global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
+template <int NRG, bool QF8, bool PLAN>
+__global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
   constexpr int QL_BYTES = QR < 9 ? ((RB * (qpitch_lds<NRG>() / 16) + 63) / 64) * 1024 : 16;
@@ -576,67 +594,89 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
   }
 
-  // ---- the split partition: T, L_max -> chunk.  The request offsets are
-  // staged in LDS (the tile buffers are still free) when they fit.
-  const bool ip_lds = (int64_t)(p.batch + 1) * 4 <= (int64_t)NBUF * TILE_BYTES;
-  MLA_LDS int32_t* ipl = (MLA_LDS int32_t*)kbuf;
-  if (ip_lds) {
-    for (int i0 = 0; i0 <= p.batch; i0 += 1024) {
-      int v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + tid + 256 * j;
-        v[j] = i <= p.batch ? p.indptr[i] : 0;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = i0 + tid + 256 * j;
-        if (i <= p.batch) ipl[i] = v[j];
-      }
-    }
-    __syncthreads();
-  }
-  auto ip = [&](int i) -> int { return ip_lds ? ipl[i] : p.indptr[i]; };
-  int lmax = 0;
-  for (int r = tid; r < p.batch; r += 256) lmax = max(lmax, ip(r + 1) - ip(r));
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) lmax = max(lmax, __shfl_xor(lmax, s));
-  if (lane == 0) red_i[wave] = lmax;
-  __syncthreads();
-  lmax = max(max(red_i[0], red_i[1]), max(red_i[2], red_i[3]));
-  const int base = ip(0);
-  // the partition's stream: request r takes MLA_PIECE_TOKENS positions, then
-  // its tokens; Vs(r) = ip(r) - base + W r is where it starts
+  // ---- the split partition: T, L_max -> chunk, and the requests this
+  // unit covers
   constexpr int64_t W = MLA_PIECE_TOKENS;
-  const int64_t Tv = (int64_t)ip(p.batch) - base + W * p.batch;
-  const int64_t chunk = split_chunk(Tv, lmax, p.num_splits, p.num_workers, p.split_min);
-  const int64_t nunits = Tv > 0 ? (Tv + chunk - 1) / chunk : 1;
-  const int64_t g0 = (int64_t)u * chunk;
-  const int64_t g1 = g0 + chunk < Tv ? g0 + chunk : Tv;
-  const bool last_unit = (u == nunits - 1);
   const int m_lo = rb * RB;  // first row (of the request's qlen*heads) of this block
-
-  // first request whose stream end is >= g0, and the requests this unit covers
-  int r = 0, r_end = 0;
-  if (u < nunits) {
-    int lo = 0, hi = p.batch;
-    while (lo < hi) {
-      int mid = (lo + hi) >> 1;
-      if ((int64_t)ip(mid + 1) - base + W * (mid + 1) >= g0) hi = mid; else lo = mid + 1;
-    }
-    r = lo;
-    r_end = r;
-    while (r_end < p.batch) {
-      const int64_t Vs = (int64_t)ip(r_end) - base + W * r_end;
-      if (Vs >= g1 && !(last_unit && Vs == Tv)) break;
-      ++r_end;
-    }
-  }
-  // (P, L) of the covered requests, read before the tile buffers are reused
   constexpr int RMAX = 64;
   __shared__ int32_t rP[RMAX + 1];
-  const int nreq = min(r_end - r, RMAX);
-  for (int i = tid; i <= nreq; i += 256) rP[i] = ip(r + i) - base;
+  __shared__ __attribute__((aligned(16))) int32_t rPraw[PLAN_RP];
+  int base = 0, r = 0, r_end = 0, nreq = 0;
+  int64_t Tv = 0, chunk = 1, nunits = 1;
+  if constexpr (PLAN) {
+    base = pl.base;
+    Tv = pl.Tv;
+    chunk = pl.chunk;
+    nunits = pl.nunits;
+    if (u < nunits) {
+      r = pl.r[u];
+      r_end = pl.r_end[u];
+      // kv_indptr[r + i] (i < PLAN_RP, clamped to the last entry) to LDS by
+      // direct loads; the first piece takes its offsets from the plan, and
+      // these loads, issued before its staging, have landed by its first wait
+      if (wave < PLAN_RP / 64) {
+        const int i = min(r + 64 * wave + lane, p.batch);
+        lds_dma4(p.indptr + i, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(rPraw + 64 * wave)));
+      }
+    }
+  } else {
+    // the request offsets are staged in LDS (the tile buffers are still
+    // free) when they fit
+    const bool ip_lds = (int64_t)(p.batch + 1) * 4 <= (int64_t)NBUF * TILE_BYTES;
+    MLA_LDS int32_t* ipl = (MLA_LDS int32_t*)kbuf;
+    if (ip_lds) {
+      for (int i0 = 0; i0 <= p.batch; i0 += 1024) {
+        int v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + tid + 256 * j;
+          v[j] = i <= p.batch ? p.indptr[i] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i0 + tid + 256 * j;
+          if (i <= p.batch) ipl[i] = v[j];
+        }
+      }
+      __syncthreads();
+    }
+    auto ip = [&](int i) -> int { return ip_lds ? ipl[i] : p.indptr[i]; };
+    int lmax = 0;
+    for (int rr = tid; rr < p.batch; rr += 256) lmax = max(lmax, ip(rr + 1) - ip(rr));
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) lmax = max(lmax, __shfl_xor(lmax, s));
+    if (lane == 0) red_i[wave] = lmax;
+    __syncthreads();
+    lmax = max(max(red_i[0], red_i[1]), max(red_i[2], red_i[3]));
+    base = ip(0);
+    // the partition's stream: request r takes MLA_PIECE_TOKENS positions,
+    // then its tokens; Vs(r) = ip(r) - base + W r is where it starts
+    Tv = (int64_t)ip(p.batch) - base + W * p.batch;
+    chunk = split_chunk(Tv, lmax, p.num_splits, p.num_workers, p.split_min);
+    nunits = Tv > 0 ? (Tv + chunk - 1) / chunk : 1;
+    const int64_t s0 = (int64_t)u * chunk;
+    const int64_t s1 = s0 + chunk < Tv ? s0 + chunk : Tv;
+    // first request whose stream end is >= s0, and the requests this unit covers
+    if (u < nunits) {
+      int lo = 0, hi = p.batch;
+      while (lo < hi) {
+        int mid = (lo + hi) >> 1;
+        if ((int64_t)ip(mid + 1) - base + W * (mid + 1) >= s0) hi = mid; else lo = mid + 1;
+      }
+      r = lo;
+      r_end = r;
+      while (r_end < p.batch) {
+        const int64_t Vs = (int64_t)ip(r_end) - base + W * r_end;
+        if (Vs >= s1 && !(u == nunits - 1 && Vs == Tv)) break;
+        ++r_end;
+      }
+    }
+    // (P, L) of the covered requests, read before the tile buffers are reused
+    nreq = min(r_end - r, RMAX);
+    for (int i = tid; i <= nreq; i += 256) rP[i] = ip(r + i) - base;
+  }
+  const int64_t g0 = (int64_t)u * chunk;
+  const int64_t g1 = g0 + chunk < Tv ? g0 + chunk : Tv;
   if (tid < RB) {
     const int m = m_lo + tid;
     rowoff[tid] = m < p.M ? (int64_t)(m / p.heads) * p.os_r + (int64_t)(m % p.heads) * p.os_h : -1;
@@ -665,10 +705,29 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
   };
 
+  bool rp_ready = !PLAN;  // the planned offsets in rPraw have landed and are visible
   for (int ri = 0; r < r_end; ++r, ++ri) {
     int64_t P;
     int L;
-    if (ri < nreq) {
+    if constexpr (PLAN) {
+      if (ri == 0) {
+        P = pl.p0[u];
+        L = pl.len0[u];
+      } else {
+        if (!rp_ready) {  // the first piece was empty: wait for the offsets here
+          wait_vm_all();
+          __syncthreads();
+          rp_ready = true;
+        }
+        if (ri + 1 < PLAN_RP) {
+          P = (int64_t)rPraw[ri] - base;
+          L = rPraw[ri + 1] - rPraw[ri];
+        } else {
+          P = (int64_t)p.indptr[r] - base;
+          L = p.indptr[r + 1] - p.indptr[r];
+        }
+      }
+    } else if (ri < nreq) {
       P = rP[ri];
       L = rP[ri + 1] - rP[ri];
     } else {
@@ -691,7 +750,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     }
 
     // ---------------------------------------------------------- one piece
-    const int32_t* rows_r = p.indices + p.indptr[r];
+    const int32_t* rows_r = p.indices + (PLAN ? base + (int)P : p.indptr[r]);
     int lim[NRG];  // visible tokens of row (g, lr), as an end in request tokens
     int lim_min = b;
 #pragma unroll
@@ -713,6 +772,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
     const int nq = stage_q_and_idx<NRG, QF8>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
+    rp_ready = true;  // the planned offsets were loaded before this staging
     {
       const int slen = min(IDX_CAP, b - a);
       const int safe_row = first_valid_row(idx, slen, p.num_slots);
@@ -957,10 +1017,52 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p) {
   }
 }
 
-template <int NRG, bool QF8>
-static int launch(const PartialArgs& a, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((partial_kernel<NRG, QF8>), dim3(blocks), dim3(256), 0, s, a);
+template <int NRG, bool QF8, bool PLAN>
+static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, int blocks, hipStream_t s) {
+  static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
+  hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN>), dim3(blocks), dim3(256), 0, s, a, pl);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// The kernel's split partition, unit by unit, on the host: the same chunk,
+// and for each unit the first request whose stream end reaches the unit's
+// start and the requests it covers (the kernel's search and scan).
+static int make_plan(const int32_t* ip, int32_t batch, int32_t num_splits, int32_t num_workers,
+                     int32_t split_min, UnitPlan<true>& pl) {
+  constexpr int64_t W = MLA_PIECE_TOKENS;
+  const int64_t base = ip[0];
+  int64_t lmax = 0;
+  for (int r = 0; r < batch; ++r) {
+    const int64_t L = (int64_t)ip[r + 1] - ip[r];
+    if (L < 0) return MLA_ERR_INVALID;
+    if (L > lmax) lmax = L;
+  }
+  const int64_t Tv = (int64_t)ip[batch] - base + W * batch;
+  const int64_t chunk = split_chunk(Tv, lmax, num_splits, num_workers, split_min);
+  const int64_t nunits = Tv > 0 ? (Tv + chunk - 1) / chunk : 1;
+  if (nunits > num_workers || nunits > PLAN_UNITS) return MLA_ERR_UNSUPPORTED;
+  pl.chunk = chunk;
+  pl.nunits = nunits;
+  pl.Tv = Tv;
+  pl.base = (int32_t)base;
+  pl.pad_ = 0;
+  int r = 0;
+  for (int64_t u = 0; u < nunits; ++u) {
+    const int64_t g0 = u * chunk, g1 = g0 + chunk < Tv ? g0 + chunk : Tv;
+    while (r < batch && (int64_t)ip[r + 1] - base + W * (r + 1) < g0) ++r;  // ends only grow with r
+    int r_end = r;
+    while (r_end < batch) {
+      const int64_t Vs = (int64_t)ip[r_end] - base + W * r_end;
+      if (Vs >= g1 && !(u == nunits - 1 && Vs == Tv)) break;
+      ++r_end;
+    }
+    pl.r[u] = r;
+    pl.r_end[u] = r_end;
+    pl.p0[u] = r < batch ? (int32_t)(ip[r] - base) : 0;
+    pl.len0[u] = r < batch ? ip[r + 1] - ip[r] : 0;
+  }
+  for (int64_t u = nunits; u < PLAN_UNITS; ++u) pl.r[u] = pl.r_end[u] = pl.p0[u] = pl.len0[u] = 0;
+  return MLA_OK;
 }
 
 }  // namespace mla
@@ -1004,7 +1106,7 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
                                int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
                                uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                                float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
-                               void* stream) {
+                               void* stream, const int32_t* indptr_host = nullptr) {
   if (batch < 0 || qlen < 1 || heads < 1 || num_splits < 1 || num_splits > 1024 || num_workers < 1)
     return MLA_ERR_INVALID;
   if (batch == 0) return MLA_OK;
@@ -1038,17 +1140,28 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   a.o = o_part; a.os_s = os_split; a.os_r = os_row; a.os_h = os_head;
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
+  if (indptr_host && !q_fp8 && num_workers <= PLAN_UNITS) {
+    UnitPlan<true> pl;
+    const int st = make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl);
+    if (st != MLA_OK) return st;
+    switch (nrg) {
+      case 1: return launch<1, false, true>(a, pl, (int)blocks, s);
+      case 2: return launch<2, false, true>(a, pl, (int)blocks, s);
+      default: return launch<3, false, true>(a, pl, (int)blocks, s);
+    }
+  }
+  const UnitPlan<false> none;
   if (q_fp8) {
     switch (nrg) {
-      case 1: return launch<1, true>(a, (int)blocks, s);
-      case 2: return launch<2, true>(a, (int)blocks, s);
-      default: return launch<3, true>(a, (int)blocks, s);
+      case 1: return launch<1, true, false>(a, none, (int)blocks, s);
+      case 2: return launch<2, true, false>(a, none, (int)blocks, s);
+      default: return launch<3, true, false>(a, none, (int)blocks, s);
     }
   }
   switch (nrg) {
-    case 1: return launch<1, false>(a, (int)blocks, s);
-    case 2: return launch<2, false>(a, (int)blocks, s);
-    default: return launch<3, false>(a, (int)blocks, s);
+    case 1: return launch<1, false, false>(a, none, (int)blocks, s);
+    case 2: return launch<2, false, false>(a, none, (int)blocks, s);
+    default: return launch<3, false, false>(a, none, (int)blocks, s);
   }
 }
 
@@ -1079,4 +1192,19 @@ extern "C" int mla_decode_partial_fp8q(const uint8_t* q8, int64_t q_stride_row, 
                                   kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
                                   ls_split, ls_row, ls_head, stream);
+}
+
+extern "C" int mla_decode_partial_hostplan(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
+                                           int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
+                                           int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                           float sm_scale, float kv_scale, int32_t num_splits,
+                                           int32_t num_workers, int32_t split_min_tokens, uint16_t* o_part,
+                                           int64_t os_split, int64_t os_row, int64_t os_head, float* lse_part,
+                                           int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                                           const int32_t* kv_indptr_host, void* stream) {
+  if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
+  return mla::decode_partial_impl(q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
+                                  num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream, kv_indptr_host);
 }

@@ -1,11 +1,13 @@
 """One decode step of the path on device buffers: kv_write -> decode_partial
 -> merge_lse -> value_gate, for a synthetic workload (see synth.py).
 
-Two variants of the same step: `use_fp8_query(q_scale)` quantises the bf16
+Variants of the same step: `use_fp8_query(q_scale)` quantises the bf16
 query with concat_quant_fp8 each step and attends on the fp8 codes
 (decode_partial with q_scale); `fused_post = True` runs merge_value_gate in
 place of merge_lse + value_gate (the value heads must be the attention
-heads).
+heads).  A bf16 query attends through mla_decode_partial_hostplan (the split
+partition built on the host from the request offsets) unless `host_plan` is
+set to False, which calls mla_decode_partial; the two give the same bits.
 
 Buffers are allocated once by `DeviceStep.__init__` (torch, on the current
 device) and reused by every `run()`, so a timed step enqueues the library
@@ -42,6 +44,8 @@ class DeviceStep:
         self.fused_post = False
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
+        self.indptr_host = np.ascontiguousarray(w.indptr, dtype=np.int32)  # the same offsets, on the host
+        self.host_plan = True
         self.indices = torch.from_numpy(w.indices).to(dev)
         self.lengths = torch.from_numpy(w.lengths).to(dev)
         if fill_cache and w.kv_rows is not None and w.total_tokens > 0:
@@ -85,9 +89,11 @@ class DeviceStep:
 
     def attend(self):
         w = self.w
+        plan = self.indptr_host if self.host_plan and self.q_scale is None else None
         decode_partial(self.q, self.kv_cache, self.indptr, self.indices, self.o_part, self.lse_part,
                        qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
-                       num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale)
+                       num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale,
+                       kv_indptr_host=plan)
 
     def merge(self):
         merge_lse(self.o_part, self.lse_part, self.latent[:, :self.w.heads], self.lse)

@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ["mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-              "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
+              "mla_decode_partial_hostplan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
 
@@ -146,3 +146,23 @@ def test_bench_step_bytes_counts_live_splits():
     assert seen <= live <= w.num_splits * w.S
     assert sb["kv_cache"] == int(w.total_tokens) * 580
     assert sb["total"] == sum(v for k, v in sb.items() if k != "total")
+
+
+def test_hostplan_argument_errors(mlib):
+    # the host-plan entry point: a null host copy of the offsets, or a
+    # decreasing one, is rejected before anything is enqueued
+    import numpy as np
+
+    L = mlib.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every case is rejected on the host
+
+    def call(ih, batch=2):
+        return L.mla_decode_partial_hostplan(fake, 576, 576, batch, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2, 8,
+                                             1, fake, 0, 0, 0, fake, 0, 0, 0, ih, null)
+
+    assert call(null) == 1
+    assert call(null, batch=0) == 0  # no requests: a no-op
+    bad = np.array([0, 5, 3], dtype=np.int32)
+    assert call(bad.ctypes.data_as(ctypes.c_void_p)) == 1
+

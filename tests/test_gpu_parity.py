@@ -392,6 +392,45 @@ def test_maximum_sizes(ops, oracle, case, monkeypatch):
     _check_merge_and_value(oracle, w, st)
 
 
+HOSTPLAN = [
+    # name, batch override, length range, num_workers, split_min
+    ("tiny", None, None, None, None),
+    ("batch", 6, (100, 700), 8, 16),      # 4 of 6 requests empty: units that start on an empty one
+    ("batch", 8, (30, 60), 32, 1),
+    ("batch", 5, (1, 70), 16, 1),
+    ("spec_q4", 3, (60, 300), 4, 16),
+    ("spec_q8", 2, (64, 200), 4, 8),
+    ("long", 2, (900, 1500), 16, 64),
+    ("rank_share", 4, (100, 500), 8, 32),
+    ("batch", 300, (1, 12), 2, 1),       # units of more than 128 requests
+    ("batch", None, None, 128, 256),     # the whole batch workload
+]
+
+
+@pytest.mark.parametrize("name,batch,lr,nw,smin", HOSTPLAN)
+def test_hostplan_is_the_in_kernel_partition_bit_for_bit(ops, name, batch, lr, nw, smin):
+    """mla_decode_partial_hostplan (the partition built on the host and passed
+    in the kernel arguments) against mla_decode_partial on the same cache:
+    every o_part and lse_part byte equal."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"host plan vs in-kernel partition: {name} batch={batch} lengths={lr} workers={nw} min={smin}")
+    w = synth.make(name, batch=batch, len_range=lr)
+    st = DeviceStep(w, num_workers=nw, split_min_tokens=smin)
+    st.write_new_tokens()
+    got = []
+    for hp in (False, True):
+        st.host_plan = hp
+        st.o_part.fill_(0)
+        st.lse_part.fill_(0)
+        st.attend()
+        torch.cuda.synchronize()
+        got.append((_np_bf16(st.o_part), st.lse_part.cpu().numpy().view(np.uint32)))
+    assert np.array_equal(got[0][1], got[1][1]), "lse_part differs"
+    assert np.array_equal(got[0][0], got[1][0]), "o_part differs"
+
+
 def test_requests_shorter_than_the_window(ops, oracle):
     """qlen 4 with requests of 1, 2, 3, 0 and 6 tokens: row j of a window
     sees max(0, L - qlen + j + 1) tokens, so the first rows of the short
