@@ -189,8 +189,9 @@ int mla_decode_partial_fp8q(const uint8_t* q8, int64_t q_stride_row, int64_t q_s
  * described at mla_decode_partial) and passes them in the kernel
  * arguments, so a workgroup starts its first piece without reading and
  * searching the offsets.  The results are bit for bit those of
- * mla_decode_partial.  Up to 192 workers; with more, the call runs as
- * mla_decode_partial.  kv_indptr_host is read during the call only.
+ * mla_decode_partial.  Up to 256 workers, and units of up to 65535
+ * requests; beyond either, the call runs as mla_decode_partial.
+ * kv_indptr_host is read during the call only.
  * Errors: those of mla_decode_partial, and MLA_ERR_INVALID for a null
  * kv_indptr_host (batch > 0) or a decreasing offset in it.
  */

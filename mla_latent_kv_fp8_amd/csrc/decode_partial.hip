@@ -66,7 +66,7 @@ struct PartialArgs {
 // kv_indptr, unit by unit), passed in the kernel arguments: a workgroup then
 // starts its first piece without first reading the request offsets and
 // searching them.
-constexpr int PLAN_UNITS = 192;  // units one plan holds (the arguments stay under 4 KB)
+constexpr int PLAN_UNITS = 256;  // units one plan holds (the arguments stay under 4 KB)
 constexpr int PLAN_RP = 128;     // request offsets of a unit staged in LDS (2 waves x 64)
 template <bool PLAN>
 struct UnitPlan {};
@@ -75,9 +75,9 @@ struct UnitPlan<true> {
   int64_t chunk, nunits, Tv;
   int32_t base, pad_;
   int32_t r[PLAN_UNITS];      // first request of unit u
-  int32_t r_end[PLAN_UNITS];  // one past its last request
   int32_t p0[PLAN_UNITS];     // kv_indptr[r] - kv_indptr[0]
   int32_t len0[PLAN_UNITS];   // L_r
+  uint16_t nreq[PLAN_UNITS];  // requests the unit covers: r .. r + nreq
 };
 
 // LDS layout of a staged tile (64 tokens x 36 chunks of 16 B): block
@@ -610,7 +610,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     nunits = pl.nunits;
     if (u < nunits) {
       r = pl.r[u];
-      r_end = pl.r_end[u];
+      r_end = r + pl.nreq[u];
       // kv_indptr[r + i] (i < PLAN_RP, clamped to the last entry) to LDS by
       // direct loads; the first piece takes its offsets from the plan, and
       // these loads, issued before its staging, have landed by its first wait
@@ -1056,12 +1056,16 @@ static int make_plan(const int32_t* ip, int32_t batch, int32_t num_splits, int32
       if (Vs >= g1 && !(u == nunits - 1 && Vs == Tv)) break;
       ++r_end;
     }
+    if (r_end - r > 0xFFFF) return MLA_ERR_UNSUPPORTED;  // the count is 16-bit
     pl.r[u] = r;
-    pl.r_end[u] = r_end;
+    pl.nreq[u] = (uint16_t)(r_end - r);
     pl.p0[u] = r < batch ? (int32_t)(ip[r] - base) : 0;
     pl.len0[u] = r < batch ? ip[r + 1] - ip[r] : 0;
   }
-  for (int64_t u = nunits; u < PLAN_UNITS; ++u) pl.r[u] = pl.r_end[u] = pl.p0[u] = pl.len0[u] = 0;
+  for (int64_t u = nunits; u < PLAN_UNITS; ++u) {
+    pl.r[u] = pl.p0[u] = pl.len0[u] = 0;
+    pl.nreq[u] = 0;
+  }
   return MLA_OK;
 }
 
@@ -1140,10 +1144,12 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   a.o = o_part; a.os_s = os_split; a.os_r = os_row; a.os_h = os_head;
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
-  if (indptr_host && !q_fp8 && num_workers <= PLAN_UNITS) {
-    UnitPlan<true> pl;
-    const int st = make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl);
-    if (st != MLA_OK) return st;
+  UnitPlan<true> pl;
+  const int st = indptr_host && !q_fp8 && num_workers <= PLAN_UNITS
+                     ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
+                     : MLA_ERR_UNSUPPORTED;
+  if (st == MLA_ERR_INVALID) return st;
+  if (st == MLA_OK) {
     switch (nrg) {
       case 1: return launch<1, false, true>(a, pl, (int)blocks, s);
       case 2: return launch<2, false, true>(a, pl, (int)blocks, s);

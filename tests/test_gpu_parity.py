@@ -404,6 +404,7 @@ HOSTPLAN = [
     ("rank_share", 4, (100, 500), 8, 32),
     ("batch", 300, (1, 12), 2, 1),       # units of more than 128 requests
     ("batch", None, None, 128, 256),     # the whole batch workload
+    ("rank_share", 64, (2048, 4096), 256, 256),  # 256 workers: the largest plan
 ]
 
 
