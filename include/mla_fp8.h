@@ -144,7 +144,7 @@ int mla_concat_quant_fp8(const uint16_t* ql_nope, int64_t ln_row, int64_t ln_hea
  * num_workers >= 1, qlen >= 1, heads >= 1.  batch = 0 is a no-op.
  * Errors: MLA_ERR_INVALID for a size outside those ranges, batch < 0, a null
  * pointer, num_slots outside [1, 2^31 - 1], or sm_scale or kv_scale not
- * positive; MLA_ERR_UNSUPPORTED unless q is 16-byte aligned with strides
+ * positive and finite; MLA_ERR_UNSUPPORTED unless q is 16-byte aligned with strides
  * that are multiples of 8, o_part is 8-byte aligned with strides that are
  * multiples of 4 and kv_cache is 16-byte aligned, or when qlen * heads
  * exceeds 2^20 or the grid (num_workers x row blocks) exceeds one launch.

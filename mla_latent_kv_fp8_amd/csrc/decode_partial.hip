@@ -1116,7 +1116,8 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (batch == 0) return MLA_OK;
   if (!q || !kv_cache || !kv_indptr || !kv_indices || !o_part || !lse_part) return MLA_ERR_INVALID;
   if (num_slots < 1 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
-  if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f)) return MLA_ERR_INVALID;
+  if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f) || kv_scale == INFINITY || sm_scale == INFINITY)
+    return MLA_ERR_INVALID;
   if (!(q_scale > 0.0f) || q_scale == INFINITY) return MLA_ERR_INVALID;
   // 16-byte query chunks (8 bf16 or 16 fp8 elements), 8-byte partial
   // stores, 16-byte cache rows

@@ -96,6 +96,10 @@ def test_argument_errors_before_device_work(mlib):
     assert L.mla_decode_partial_fp8q(*args(float("nan"), 576)) == 1
     assert L.mla_decode_partial_fp8q(*args(float("inf"), 576)) == 1
     assert L.mla_decode_partial_fp8q(*args(0.5, 584)) == 2            # fp8 row stride not 16-B aligned
+    sc = lambda sm, kv: (fake, 576, 576, 2, 1, 16, fake, 10, fake, fake, sm, kv, 2, 8, 1, fake, 0, 0, 0, fake, 0,
+                         0, 0, null)
+    for sm, kv in ((float("inf"), 1.0), (0.1, float("inf")), (float("nan"), 1.0), (0.1, -1.0)):
+        assert L.mla_decode_partial(*sc(sm, kv)) == 1                 # scales must be positive and finite
     cq = lambda qs, lr, rows: (fake, lr, 512, fake, 192 * 4, 192, qs, rows, 4, fake, 2304, 576, null)
     assert L.mla_concat_quant_fp8(*cq(0.5, 2048, 0)) == 0            # rows = 0: no-op
     assert L.mla_concat_quant_fp8(null, 2048, 512, null, 768, 192, 0.5, 2, 4, null, 2304, 576, null) == 1
