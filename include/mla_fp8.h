@@ -12,8 +12,8 @@
  *   mla_decode_partial  absorbed queries attend over the paged fp8 cache:
  *                       split-KV partials o (bf16) and LSE (f32)
  *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
- *   mla_decode_partial_hostplan  mla_decode_partial with the split partition
- *                       computed on the host
+ *   mla_decode_partial_hostplan, mla_decode_partial_fp8q_hostplan  the two
+ *                       above with the split partition computed on the host
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
  *   mla_merge_value_gate  the merge, W_UV and gate in one call (no latent written)
@@ -203,6 +203,22 @@ int mla_decode_partial_hostplan(const uint16_t* q, int64_t q_stride_row, int64_t
                                 int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split,
                                 int64_t ls_row, int64_t ls_head, const int32_t* kv_indptr_host,
                                 void* stream);
+
+/*
+ * mla_decode_partial_fp8q with the split partition computed on the host, as
+ * mla_decode_partial_hostplan does for a bf16 query: the same arguments,
+ * outputs and errors as mla_decode_partial_fp8q, plus kv_indptr_host
+ * [batch+1] int32 (HOST), under the same rules.  The results are bit for
+ * bit those of mla_decode_partial_fp8q.
+ */
+int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_stride_row, int64_t q_stride_head,
+                                     float q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                                     const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                                     const int32_t* kv_indices, float sm_scale, float kv_scale,
+                                     int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                                     uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                                     float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                                     const int32_t* kv_indptr_host, void* stream);
 
 /*
  * Host helper: the split partition mla_decode_partial uses.

@@ -45,6 +45,9 @@ def lib() -> ctypes.CDLL:
                                          i32, P, i64, i64, i64, P, i64, i64, i64, P]
         L.mla_decode_partial_hostplan.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32,
                                                   i32, i32, P, i64, i64, i64, P, i64, i64, i64, P, P]
+        L.mla_decode_partial_fp8q_hostplan.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32,
+                                                       f32, i32, i32, i32, P, i64, i64, i64, P, i64, i64,
+                                                       i64, P, P]
         L.mla_concat_quant_fp8.argtypes = [P, i64, i64, P, i64, i64, f32, i32, i32, P, i64, i64, P]
         L.mla_decode_partial_fp8q.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32, f32,
                                               i32, i32, i32, P, i64, i64, i64, P, i64, i64, i64, P]
@@ -56,7 +59,7 @@ def lib() -> ctypes.CDLL:
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-                     "mla_decode_partial_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate"):
+                     "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -124,8 +127,8 @@ def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Ten
     -> o_part [splits, S, heads, 512] bf16, lse_part [splits, S, heads] f32
     (strided views allowed).  q is bf16, or fp8 E4M3 codes (uint8 or
     float8_e4m3fn) standing for q_scale * fp8(q), which then must be given.
-    kv_indptr_host (bf16 query only): a host copy of kv_indptr, from which
-    mla_decode_partial_hostplan computes the split partition on the host."""
+    kv_indptr_host: a host copy of kv_indptr, from which the *_hostplan entry
+    points compute the split partition on the host."""
     S = q.shape[0]
     batch = kv_indptr.shape[0] - 1
     if S != batch * qlen:
@@ -144,15 +147,19 @@ def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Ten
             _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
             _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
             lse_part.stride(2), _stream())
-    if fp8_q:
-        if kv_indptr_host is not None:
-            raise MlaError("the host-built partition is for a bf16 query")
-        st = lib().mla_decode_partial_fp8q(_dev(q, "q", _U8), q.stride(0), q.stride(1), float(q_scale), *rest)
-        _check(st, "mla_decode_partial_fp8q")
-    elif kv_indptr_host is not None:
+    ih = None
+    if kv_indptr_host is not None:
         ih = np.ascontiguousarray(kv_indptr_host, dtype=np.int32)
         if ih.shape != (batch + 1,):
             raise MlaError("kv_indptr_host must hold batch+1 offsets")
+    if fp8_q and ih is not None:
+        st = lib().mla_decode_partial_fp8q_hostplan(_dev(q, "q", _U8), q.stride(0), q.stride(1), float(q_scale),
+                                                    *rest[:-1], ih.ctypes.data_as(ctypes.c_void_p), rest[-1])
+        _check(st, "mla_decode_partial_fp8q_hostplan")
+    elif fp8_q:
+        st = lib().mla_decode_partial_fp8q(_dev(q, "q", _U8), q.stride(0), q.stride(1), float(q_scale), *rest)
+        _check(st, "mla_decode_partial_fp8q")
+    elif ih is not None:
         st = lib().mla_decode_partial_hostplan(_dev(q, "q", _BF16), q.stride(0), q.stride(1), *rest[:-1],
                                                ih.ctypes.data_as(ctypes.c_void_p), rest[-1])
         _check(st, "mla_decode_partial_hostplan")
@@ -164,8 +171,9 @@ def decode_partial(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Ten
 def decode_partial_hostplan(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,
                             kv_indices: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor,
                             kv_indptr_host: np.ndarray, **kw) -> None:
-    """mla_decode_partial_hostplan: decode_partial for a bf16 query, with the
-    split partition computed on the host from kv_indptr_host."""
+    """mla_decode_partial_hostplan / mla_decode_partial_fp8q_hostplan:
+    decode_partial with the split partition computed on the host from
+    kv_indptr_host."""
     decode_partial(q, kv_cache, kv_indptr, kv_indices, o_part, lse_part, kv_indptr_host=kv_indptr_host, **kw)
 
 

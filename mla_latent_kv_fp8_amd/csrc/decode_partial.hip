@@ -1146,11 +1146,18 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
   UnitPlan<true> pl;
-  const int st = indptr_host && !q_fp8 && num_workers <= PLAN_UNITS
+  const int st = indptr_host && num_workers <= PLAN_UNITS
                      ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
                      : MLA_ERR_UNSUPPORTED;
   if (st == MLA_ERR_INVALID) return st;
   if (st == MLA_OK) {
+    if (q_fp8) {
+      switch (nrg) {
+        case 1: return launch<1, true, true>(a, pl, (int)blocks, s);
+        case 2: return launch<2, true, true>(a, pl, (int)blocks, s);
+        default: return launch<3, true, true>(a, pl, (int)blocks, s);
+      }
+    }
     switch (nrg) {
       case 1: return launch<1, false, true>(a, pl, (int)blocks, s);
       case 2: return launch<2, false, true>(a, pl, (int)blocks, s);
@@ -1212,6 +1219,22 @@ extern "C" int mla_decode_partial_hostplan(const uint16_t* q, int64_t q_stride_r
   if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
   return mla::decode_partial_impl(q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
                                   num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream, kv_indptr_host);
+}
+
+extern "C" int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_stride_row, int64_t q_stride_head,
+                                                float q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                                                const uint8_t* kv_cache, int64_t num_slots,
+                                                const int32_t* kv_indptr, const int32_t* kv_indices,
+                                                float sm_scale, float kv_scale, int32_t num_splits,
+                                                int32_t num_workers, int32_t split_min_tokens, uint16_t* o_part,
+                                                int64_t os_split, int64_t os_row, int64_t os_head,
+                                                float* lse_part, int64_t ls_split, int64_t ls_row,
+                                                int64_t ls_head, const int32_t* kv_indptr_host, void* stream) {
+  if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
+  return mla::decode_partial_impl(q8, true, q_stride_row, q_stride_head, q_scale, batch, qlen, heads,
+                                  kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
                                   ls_split, ls_row, ls_head, stream, kv_indptr_host);
 }

@@ -5,9 +5,10 @@ Variants of the same step: `use_fp8_query(q_scale)` quantises the bf16
 query with concat_quant_fp8 each step and attends on the fp8 codes
 (decode_partial with q_scale); `fused_post = True` runs merge_value_gate in
 place of merge_lse + value_gate (the value heads must be the attention
-heads).  A bf16 query attends through mla_decode_partial_hostplan (the split
+heads).  The partials come from the *_hostplan entry points (the split
 partition built on the host from the request offsets) unless `host_plan` is
-set to False, which calls mla_decode_partial; the two give the same bits.
+set to False, which calls mla_decode_partial(_fp8q); the two give the same
+bits.
 
 Buffers are allocated once by `DeviceStep.__init__` (torch, on the current
 device) and reused by every `run()`, so a timed step enqueues the library
@@ -89,7 +90,7 @@ class DeviceStep:
 
     def attend(self):
         w = self.w
-        plan = self.indptr_host if self.host_plan and self.q_scale is None else None
+        plan = self.indptr_host if self.host_plan else None
         decode_partial(self.q, self.kv_cache, self.indptr, self.indices, self.o_part, self.lse_part,
                        qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
                        num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale,

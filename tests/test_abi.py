@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for n in ["mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-              "mla_decode_partial_hostplan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
+              "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
 
@@ -167,6 +167,8 @@ def test_hostplan_argument_errors(mlib):
 
     assert call(null) == 1
     assert call(null, batch=0) == 0  # no requests: a no-op
+    assert L.mla_decode_partial_fp8q_hostplan(fake, 576, 576, 0.5, 2, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2,
+                                              8, 1, fake, 0, 0, 0, fake, 0, 0, 0, null, null) == 1
     bad = np.array([0, 5, 3], dtype=np.int32)
     assert call(bad.ctypes.data_as(ctypes.c_void_p)) == 1
 

@@ -432,6 +432,31 @@ def test_hostplan_is_the_in_kernel_partition_bit_for_bit(ops, name, batch, lr, n
     assert np.array_equal(got[0][0], got[1][0]), "o_part differs"
 
 
+@pytest.mark.parametrize("name,batch,lr,nw,smin", [HOSTPLAN[1], HOSTPLAN[4], HOSTPLAN[8], HOSTPLAN[9]])
+def test_hostplan_fp8_query_is_the_in_kernel_partition_bit_for_bit(ops, name, batch, lr, nw, smin):
+    """mla_decode_partial_fp8q_hostplan against mla_decode_partial_fp8q on the
+    same fp8 query and cache: every o_part and lse_part byte equal."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"host plan vs in-kernel partition, fp8 query: {name} batch={batch} lengths={lr} workers={nw}")
+    w = synth.make(name, batch=batch, len_range=lr)
+    st = DeviceStep(w, num_workers=nw, split_min_tokens=smin)
+    q8, q_scale = synth.fp8_query(np.random.default_rng(7), w.q.shape, w.heads)
+    st.q, st.q_scale = torch.from_numpy(q8).cuda(), q_scale
+    st.write_new_tokens()
+    got = []
+    for hp in (False, True):
+        st.host_plan = hp
+        st.o_part.fill_(0)
+        st.lse_part.fill_(0)
+        st.attend()
+        torch.cuda.synchronize()
+        got.append((_np_bf16(st.o_part), st.lse_part.cpu().numpy().view(np.uint32)))
+    assert np.array_equal(got[0][1], got[1][1]), "lse_part differs"
+    assert np.array_equal(got[0][0], got[1][0]), "o_part differs"
+
+
 def test_requests_shorter_than_the_window(ops, oracle):
     """qlen 4 with requests of 1, 2, 3, 0 and 6 tokens: row j of a window
     sees max(0, L - qlen + j + 1) tokens, so the first rows of the short
