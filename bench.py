@@ -34,8 +34,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="batch")
     ap.add_argument("--fp8-query", action="store_true",
                     help="the fp8-query path: each step quantises the bf16 query to fp8 E4M3 with a "
