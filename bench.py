@@ -46,9 +46,6 @@ def parse():
                          "or as one call (mla_merge_value_gate; needs value heads == attention heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--gather-probe", action="store_true",
-                    help="only time a plain read of the workload's cache rows (libmla_probe.so), cold, as "
-                         "the practical HBM ceiling of the partial kernel's gather pattern")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
                          "kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -78,48 +75,6 @@ def copy_probe():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
-
-
-def gather_probe(config, steps):
-    """Cold-cache rate of a kernel that only reads the workload's cache rows
-    (in page-table order, and sorted), with the bench's own eviction."""
-    import ctypes
-
-    import torch
-
-    from mla_latent_kv_fp8_amd import synth
-
-    here = os.path.dirname(os.path.abspath(__file__))
-    L = ctypes.CDLL(os.path.join(here, "mla_latent_kv_fp8_amd", "libmla_probe.so"))
-    L.mla_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                   ctypes.c_int32, ctypes.c_void_p]
-    L.mla_probe_gather.restype = ctypes.c_int
-    w = synth.make(config, draw_kv=False)
-    kv = torch.zeros((w.num_slots, 576), dtype=torch.uint8, device="cuda")
-    evict = Evict(torch)
-    grid = 4096
-    out = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
-    res = {"probe": "plain gather of the workload's cache rows, cold", "workload": config,
-           "bytes": int(w.total_tokens) * 576}
-    for order in ("page_table", "sorted"):
-        idx = np.sort(w.indices) if order == "sorted" else w.indices
-        ids = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
-        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        ev = []
-        for _ in range(steps):
-            evict()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            rc = L.mla_probe_gather(kv.data_ptr(), ids.data_ptr(), ids.numel(), out.data_ptr(), grid, s)
-            b.record()
-            if rc != 0:
-                raise RuntimeError("mla_probe_gather failed (%d)" % rc)
-            ev.append((a, b))
-        torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
-        res[order] = {"us": round(us, 2), "GB/s": round(res["bytes"] / us / 1e3, 1),
-                      "frac_of_8TBs": round(res["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4)}
-    print(json.dumps(res))
 
 
 def algorithmic(w):
@@ -234,9 +189,6 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
-        return
-    if args.gather_probe:
-        gather_probe(args.config, max(args.steps, 5))
         return
     import torch
 

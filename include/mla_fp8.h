@@ -191,9 +191,15 @@ int mla_decode_partial_fp8q(const uint8_t* q8, int64_t q_stride_row, int64_t q_s
  * searching the offsets.  The results are bit for bit those of
  * mla_decode_partial.  Up to 256 workers, and units of up to 65535
  * requests; beyond either, the call runs as mla_decode_partial.
- * kv_indptr_host is read during the call only.
+ * kv_indptr_host is read during the call only.  It must hold exactly the
+ * offsets of kv_indptr: a host copy that differs is undefined behaviour
+ * (the first piece of a unit takes its range from the host copy and could
+ * read kv_indices outside the request).  A split index that the mismatch
+ * would push past num_splits is never written: that piece sets LSE NaN in
+ * split num_splits-1 of its rows instead.
  * Errors: those of mla_decode_partial, and MLA_ERR_INVALID for a null
- * kv_indptr_host (batch > 0) or a decreasing offset in it.
+ * kv_indptr_host (batch > 0) or a decreasing offset in it (checked for any
+ * worker count).
  */
 int mla_decode_partial_hostplan(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
                                 int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,

@@ -22,7 +22,9 @@ D_LATENT, D_ROPE, D_QK, D_V = 512, 64, 576, 128
 W_BF16, W_MXFP4 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla_fp8.so")
+# MLA_FP8_LIBRARY names another build of the same library (the host-code
+# sanitizer build of the CPU tests); the default is the in-tree build
+LIB_PATH = os.environ.get("MLA_FP8_LIBRARY") or os.path.join(_HERE, "libmla_fp8.so")
 _lib = None
 
 

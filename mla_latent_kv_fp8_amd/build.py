@@ -12,9 +12,6 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_fp8.so")
-# measurement probe (bench.py --gather-probe), a library of its own: not the path's C ABI
-PROBE_LIB = os.path.join(HERE, "libmla_probe.so")
-PROBE_SRC = "probe_gather.hip"
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["kv_write.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip", "merge_value.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,32 +22,41 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# host code (argument checks, the host-built split partition, launches)
+# instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; the
+# device code is built as usual
+SANITIZE_FLAGS = ["-g", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+                  "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
+SANITIZED_LIB = os.path.join(BUILD_DIR, "asan", "libmla_fp8_asan.so")
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    out_dir = os.path.join(BUILD_DIR, "asan") if sanitize else BUILD_DIR
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
     return obj
 
 
-def build() -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(sanitize: bool = False) -> str:
+    """Build the library in-tree, or (sanitize=True) the host-sanitizer build
+    under _build/asan, which a process loads with the clang ASan runtime
+    preloaded."""
+    out = SANITIZED_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(out) if sanitize else BUILD_DIR, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    r = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp],
+        objs = list(ex.map(lambda src: _compile(src, sanitize), SOURCES))
+    tmp = out + ".tmp%d" % os.getpid()
+    link_san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-shared-libsan"] if sanitize else []
+    r = subprocess.run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *link_san, *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, LIB)
-    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
-    r = subprocess.run([HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SRC), "-o", tmp],
-                       capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s" % (PROBE_SRC, r.stderr))
-    os.replace(tmp, PROBE_LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

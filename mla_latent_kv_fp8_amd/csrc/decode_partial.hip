@@ -744,6 +744,17 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     const int b = (int)((g1 < V + L ? g1 : V + L) - V);
     if (b <= a) continue;
     const int k = (a == 0) ? 0 : (int)((V + a) / chunk - V / chunk);
+    if (PLAN && k >= p.num_splits) {
+      // only a host copy of the offsets that differs from kv_indptr gets
+      // here: poison the rows' last split instead of writing past it
+      const int nrows = min(RB, p.M - m_lo);
+      if (tid < nrows) {
+        const int m = m_lo + tid;
+        p.lse[(int64_t)(p.num_splits - 1) * p.ls_s + (int64_t)(r * p.qlen + m / p.heads) * p.ls_r +
+              (int64_t)(m % p.heads) * p.ls_h] = __builtin_nanf("");
+      }
+      continue;
+    }
     if (k == 0) {
       const int nsplit = (int)((V + L - 1) / chunk - V / chunk + 1);
       if (nsplit < p.num_splits) fill_neginf(r, nsplit);
@@ -1146,6 +1157,9 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
   UnitPlan<true> pl;
+  if (indptr_host)
+    for (int32_t r = 0; r < batch; ++r)
+      if (indptr_host[r + 1] < indptr_host[r]) return MLA_ERR_INVALID;
   const int st = indptr_host && num_workers <= PLAN_UNITS
                      ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
                      : MLA_ERR_UNSUPPORTED;

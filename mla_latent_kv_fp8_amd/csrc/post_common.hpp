@@ -164,9 +164,9 @@ __device__ __forceinline__ void load_w_frags(const void* w_uv, int64_t w_head, i
   }
 }
 
-// Gate epilogue for one lane's four outputs (C rows 4lg..4lg+3): bf16 value
-// times the FP32 sigmoid of the bf16 logit, rounded to bf16; +0 for a row of
-// an empty request (len == 0), whatever the gate holds.
+// Gate epilogue for one lane's four outputs (C rows 4lg..4lg+3):
+// len > 0 ? bf16(f32(bf16(acc)) * sigma_f32(f32(g))) : +0 (a NaN gate or
+// value of an empty request's row is not propagated).
 __device__ __forceinline__ u32x2 gate_out(const f32x4& acc, const u32x2& gv, int len) {
   if (len <= 0) return u32x2{0, 0};
   float o[4];

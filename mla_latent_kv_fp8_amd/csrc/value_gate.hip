@@ -1,6 +1,7 @@
-// W_UV value projection fused with the FP32 sigmoid gate (the value step of
-// the decode runtime's `post`; MlaValue / MlaGate semantics: bf16 value times
-// the FP32 sigmoid, rounded to bf16; rows of empty requests are +0).
+// W_UV value projection fused with the gate epilogue (the value step of the
+// decode runtime's `post`; the gate rule of the CuTe-DSL value page, classes
+// MlaValue and MlaGate):  out = len_r > 0 ? bf16(f32(bf16(acc)) * sigma_f32(g))
+// : +0, with acc = sum_l latent[l] * W[v][l].
 #include "post_common.hpp"
 
 namespace mla {

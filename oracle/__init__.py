@@ -22,8 +22,24 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mla_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_ASAN_LIB_PATH = os.path.join(_HERE, "liboracle_asan.so")
+# MLA_ORACLE_LIBRARY names a prebuilt oracle to load instead (the
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the CPU tests)
+_LIB_OVERRIDE = os.environ.get("MLA_ORACLE_LIBRARY")
 
 D_LATENT, D_ROPE, D_QK, D_V = 512, 64, 576, 128
+
+
+def build_sanitized() -> str:
+    """The oracle built with gcc's AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts); load it into a process that preloads libasan."""
+    tmp = _ASAN_LIB_PATH + ".tmp%d" % os.getpid()
+    subprocess.check_call(
+        ["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+         "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+         _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _ASAN_LIB_PATH)
+    return _ASAN_LIB_PATH
 
 
 def build(force: bool = True) -> str:
@@ -43,9 +59,13 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB_PATH)
+        if _LIB_OVERRIDE:
+            path = _LIB_OVERRIDE
+        else:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+            path = _LIB_PATH
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f32, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double
         L.orc_fp8_decode.argtypes = [ctypes.c_uint8]

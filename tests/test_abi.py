@@ -172,3 +172,43 @@ def test_hostplan_argument_errors(mlib):
     bad = np.array([0, 5, 3], dtype=np.int32)
     assert call(bad.ctypes.data_as(ctypes.c_void_p)) == 1
 
+
+
+def test_hostplan_partition_runs_on_the_host(mlib):
+    # Valid calls of the host-plan entry points reach the host-built split
+    # partition (argument checks, the partition, the kernel arguments) and
+    # only then the launch, which fails without a device: status 3.  This
+    # runs the host code over many shapes (and under the sanitizer build, in
+    # test_sanitizers.py).  Only without a visible GPU: the device pointers
+    # here are fakes.
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible: the fake device pointers must not reach a launch")
+    L = mlib.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)
+    rng = np.random.default_rng(11)
+    for it in range(60):
+        B = int(rng.integers(1, 400))
+        lens = rng.integers(0, 20000, B)
+        lens[rng.random(B) < 0.1] = 0
+        ih = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        nw = int(rng.choice([1, 7, 64, 128, 256, 300]))
+        ns = int(rng.integers(1, 65))
+        for fp8 in (False, True):
+            if fp8:
+                st = L.mla_decode_partial_fp8q_hostplan(fake, 576, 576, 0.5, B, 1, 16, fake, 1 << 30, fake, fake,
+                                                        0.1, 1.0, ns, nw, 256, fake, 0, 0, 0, fake, 0, 0, 0,
+                                                        ih.ctypes.data_as(ctypes.c_void_p), null)
+            else:
+                st = L.mla_decode_partial_hostplan(fake, 576, 576, B, 1, 96, fake, 1 << 30, fake, fake, 0.1, 1.0,
+                                                   ns, nw, 256, fake, 0, 0, 0, fake, 0, 0, 0,
+                                                   ih.ctypes.data_as(ctypes.c_void_p), null)
+            assert st == 3, (it, st)
+    # a decreasing host offset is refused for any worker count
+    bad = np.array([0, 5, 3], dtype=np.int32)
+    for nw in (8, 256, 300, 4096):
+        assert L.mla_decode_partial_hostplan(fake, 576, 576, 2, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2, nw, 1,
+                                             fake, 0, 0, 0, fake, 0, 0, 0, bad.ctypes.data_as(ctypes.c_void_p),
+                                             null) == 1

@@ -577,9 +577,86 @@ def test_value_gate_parity(ops, oracle, fmt, rows, qlen, heads):
     assert (got[empty] == 0).all()
     g, r = oracle.bf16_decode(got[~empty]), oracle.bf16_decode(ref[~empty])
     assert np.abs(g - r).max() <= OUT_REL_TOL * np.abs(r).max()
-    # gate logit 0 -> exactly half of the bf16 value (GPU value = own bf16(acc))
+    # gate logit 0: sigma = 1/2 exactly, so out = bf16(acc) / 2 with no second
+    # rounding.  The GPU accumulates in f32 in its own order, so bf16(acc)
+    # is compared bit for bit where the oracle's exact acc lies farther from
+    # a bf16 rounding midpoint than any f32 accumulation error can move it
+    # (2^-18 of the sum of |terms|: 16 K-steps of 32 exact products each
+    # add at most about 2^-19 of it), and within one bf16 ulp elsewhere.
+    acc0 = acc[~empty][:, :7]
+    if fmt == "bf16":
+        w_dec = oracle.bf16_decode(wuv)
+    else:
+        w_dec = (oracle.e2m1_decode(np.stack([w4 & 15, w4 >> 4], -1).reshape(heads, 128, 512))
+                 * np.repeat(oracle.e8m0_decode(ws), 32, axis=-1))
+    lat_ne = oracle.bf16_decode(lat[~empty])
+    abs_terms = np.abs(lat_ne[:, 0]) @ np.abs(w_dec[0, :7]).T  # head 0, outputs 0..6
+    want = oracle.bf16_round(oracle.bf16_decode(oracle.bf16_round(acc0)) * 0.5)
     half = got[~empty][:, :7]
-    assert np.all(np.isfinite(oracle.bf16_decode(half)))
+    mag = np.abs(acc0)
+    ulp = 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7)
+    frac = mag / ulp - np.floor(mag / ulp)
+    far = np.abs(frac - 0.5) * ulp > 2.0 ** -18 * abs_terms
+    assert far.mean() > 0.5  # the exact check covers most entries
+    assert np.array_equal(half[far], want[far])
+    near_err = np.abs(oracle.bf16_decode(half[~far]) - oracle.bf16_decode(want[~far]))
+    assert np.all(near_err <= ulp[~far] / 2 * 1.0000001)
+
+
+def test_value_gate_mxfp4_edge_scales(ops, oracle):
+    """MXFP4 W_UV with E8M0 scale bytes at the edges of the format, against
+    the oracle's exact decode (e2m1 * 2^(s-127)):
+      head 0: every scale 0x00 (2^-127, so most decoded weights are bf16
+              subnormals), latent scaled by 2^100;
+      head 1: some 32-element blocks with scale 0xFF (NaN): exactly the
+              outputs whose weight row holds such a block are NaN (rows of
+              non-empty requests), all others finite;
+      head 2: scales 250 and 252 (weights up to 6 * 2^125, the largest that
+              bf16 holds for every code), latent scaled by 2^-110;
+      head 3: scales drawn over [1, 200] per block, a plain latent.
+    Each head is compared against its own largest reference output."""
+    from mla_latent_kv_fp8_amd.synth import to_bf16_bits, BF16_NAN
+
+    _announce("value_gate mxfp4 edge scales")
+    rng = np.random.default_rng(4242)
+    heads, qlen, B = 4, 1, 24
+    rows = B * qlen
+    lengths = rng.integers(1, 5, B).astype(np.int32)
+    lengths[3] = 0
+    latf = rng.standard_normal((rows, heads, 512)) * 0.3
+    latf[:, 0] *= 2.0 ** 100
+    latf[:, 2] *= 2.0 ** -110
+    lat = to_bf16_bits(latf.astype(np.float32))
+    gate = to_bf16_bits(rng.standard_normal((rows, heads * 128)).astype(np.float32))
+    empty = np.repeat(lengths == 0, qlen)
+    gate[empty] = BF16_NAN
+    w4 = rng.integers(0, 256, (heads, 128, 256), dtype=np.uint8)
+    ws = np.empty((heads, 128, 16), np.uint8)
+    ws[0] = 0
+    ws[1] = rng.integers(118, 125, (128, 16))
+    nan_blocks = rng.random((128, 16)) < 0.03
+    nan_blocks[5, 3] = True
+    ws[1][nan_blocks] = 0xFF
+    ws[2] = rng.choice(np.array([250, 252], np.uint8), (128, 16))
+    ws[3] = rng.integers(1, 201, (128, 16))
+    out = torch.full((rows, heads * 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.value_gate(_bf16_dev(lat), _bf16_dev(gate), torch.from_numpy(lengths).cuda(), out, qlen=qlen,
+                   w_fp4=torch.from_numpy(w4).cuda(), w_scale=torch.from_numpy(ws).cuda())
+    _, ref = oracle.value_gate(lat, gate, lengths, qlen, w_fp4=w4, w_scale=ws)
+    torch.cuda.synchronize()
+    got = _np_bf16(out)
+    assert (got[empty] == 0).all()
+    g = oracle.bf16_decode(got[~empty]).reshape(-1, heads, 128)
+    r = oracle.bf16_decode(ref[~empty]).reshape(-1, heads, 128)
+    nan_rows = nan_blocks.any(axis=1)  # output v of head 1 is NaN
+    assert np.array_equal(np.isnan(r[:, 1]), np.broadcast_to(nan_rows, r[:, 1].shape))
+    assert np.array_equal(np.isnan(g), np.isnan(r))
+    for h in range(heads):
+        fin = ~np.isnan(r[:, h])
+        assert np.all(np.isfinite(g[:, h][fin])), h
+        scale = np.abs(r[:, h][fin]).max()
+        assert scale > 0, h
+        assert np.abs(g[:, h][fin] - r[:, h][fin]).max() <= OUT_REL_TOL * scale, h
 
 
 # ------------------------------------------- fused merge + value + gate
@@ -766,8 +843,9 @@ def test_single_split_and_one_token(ops, oracle):
 
 # ------------------------------------------- full size, sampled (bench launch)
 
-@pytest.mark.parametrize("name,fp8_q", [("batch", None), ("long", None), ("spec_q8", None),
-                                         ("rank_share", None), ("batch", "codes"), ("batch", "quantised")])
+@pytest.mark.parametrize("name,fp8_q", [("batch", None), ("batch_8k", None), ("long", None), ("spec_q4", None),
+                                         ("spec_q8", None), ("rank_share", None), ("batch", "codes"),
+                                         ("batch", "quantised"), ("spec_q8", "codes"), ("long", "codes")])
 def test_full_size_sampled(ops, oracle, name, fp8_q):
     """The bench configuration at full size; the oracle recomputes a few
     sampled requests (their cache rows written by the oracle itself).  With
