@@ -22,6 +22,11 @@ FLAGS = [
 ]
 
 
+# per-source flags: the partial kernel keeps its query in accumulation
+# registers and its MFMA accumulators (O, S) in arch registers, which the
+# compiler's default heuristic does not choose for it
+SOURCE_FLAGS = {"decode_partial.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
 # host code (argument checks, the host-built split partition, launches)
 # instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; the
 # device code is built as usual
@@ -33,7 +38,8 @@ SANITIZED_LIB = os.path.join(BUILD_DIR, "asan", "libmla_fp8_asan.so")
 def _compile(src: str, sanitize: bool = False) -> str:
     out_dir = os.path.join(BUILD_DIR, "asan") if sanitize else BUILD_DIR
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *(SANITIZE_FLAGS if sanitize else []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *(SANITIZE_FLAGS if sanitize else []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))

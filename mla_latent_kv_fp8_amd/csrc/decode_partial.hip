@@ -177,10 +177,17 @@ constexpr int NBUF = 3;        // staged tiles in flight (triple buffering)
 #ifndef QPIN3
 #define QPIN3 9
 #endif
-// K-step pairs (64 dims each) of the query held in registers; the rest is
-// read from LDS every tile (only the 48-row block needs that, to fit O and
-// the query fragments in the 256 accumulation registers)
-template <int NRG> constexpr int qreg_pairs() { return NRG >= 3 ? QREG3 : 9; }
+// K-step pairs (64 dims each) of a bf16 query block staged in the staging
+// area (tile buffer 2); the 48-row block's other pairs are staged in the
+// query area of LDS at the same time, since 48 rows do not fit one buffer
+template <int NRG> constexpr int qstage_pairs() { return NRG >= 3 ? QREG3 : 9; }
+#ifndef MLA_QALL
+#define MLA_QALL 1
+#endif
+// K-step pairs of the query held in registers for the whole piece: all of
+// them, read once per piece from the two staging areas (with MLA_QALL 0 the
+// 48-row block instead reads the pairs past qstage_pairs from LDS every tile)
+template <int NRG> constexpr int qreg_pairs() { return MLA_QALL ? 9 : qstage_pairs<NRG>(); }
 
 // max over the 4 lane groups {l, l^16, l^32, l^48} with VALU lane swaps
 __device__ __forceinline__ float group_max4(float x) {
@@ -238,14 +245,15 @@ __device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int
 // plus one chunk of padding (which staggers the rows over the LDS banks)
 // where the block still fits the one tile buffer it is staged in.
 template <int NRG> constexpr int qw_reg() {
-  return 16 * NRG * (8 * qreg_pairs<NRG>() + 1) <= TILE_BYTES / 16 ? 8 * qreg_pairs<NRG>() + 1 : 8 * qreg_pairs<NRG>();
+  return 16 * NRG * (8 * qstage_pairs<NRG>() + 1) <= TILE_BYTES / 16 ? 8 * qstage_pairs<NRG>() + 1
+                                                                       : 8 * qstage_pairs<NRG>();
 }
 template <int NRG> constexpr int qpitch_reg() { return 16 * qw_reg<NRG>(); }
 // The LDS part holds, per row, 8 chunks per K-step pair in the order the
 // QK reads them (chunk 4h + lg of a pair: dims 16lg + 8h .. +7 of it, so
 // one read instruction covers 64 contiguous bytes of each row), plus two
 // chunks of padding: a 544-byte pitch (48 rows) has no bank conflicts.
-template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qreg_pairs<NRG>()) + 2); }
+template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qstage_pairs<NRG>()) + 2); }
 
 // An fp8 query block is staged whole, as its natural rows of 576 bytes
 // (36 chunks of 16 B) at qreg + 576 i; decode_q8 turns it into bf16 once per
@@ -257,7 +265,7 @@ __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int 
                                                int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
                                                MLA_LDS int32_t* idx_lds, int wave, int lane) {
   constexpr int RB = 16 * NRG;
-  constexpr int QR = qreg_pairs<NRG>();
+  constexpr int QR = qstage_pairs<NRG>();
   // the indices go first: the caller waits for them alone and issues the
   // first tiles while the query is still in flight
   stage_idx(idx_src, nidx, idx_lds, wave, lane);
@@ -557,7 +565,8 @@ template <int NRG, bool QF8, bool PLAN>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl) {
   constexpr int RB = 16 * NRG;
   constexpr int QR = qreg_pairs<NRG>();
-  constexpr int QL_BYTES = QR < 9 ? ((RB * (qpitch_lds<NRG>() / 16) + 63) / 64) * 1024 : 16;
+  constexpr int QS = qstage_pairs<NRG>();
+  constexpr int QL_BYTES = QS < 9 && !(QF8 && QR == 9) ? ((RB * (qpitch_lds<NRG>() / 16) + 63) / 64) * 1024 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
@@ -810,9 +819,17 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       for (int g = 0; g < NRG; ++g) {
         const MLA_LDS uint8_t* src = qst + (16 * g + lr) * qpitch_reg<NRG>() + 32 * lg;
 #pragma unroll
-        for (int pp = 0; pp < QR; ++pp) {
+        for (int pp = 0; pp < (QR < QS ? QR : QS); ++pp) {
           qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src + 128 * pp);
           qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src + 128 * pp + 16);
+        }
+        // pairs staged in the query area (read order: chunk 4h + lg of a
+        // pair holds dims 16lg + 8h .. +7 of it)
+        const MLA_LDS uint8_t* src2 = qlds + (16 * g + lr) * qpitch_lds<NRG>() + 16 * lg;
+#pragma unroll
+        for (int pp = QS; pp < QR; ++pp) {
+          qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src2 + 128 * (pp - QS));
+          qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src2 + 128 * (pp - QS) + 64);
         }
       }
     }
