@@ -94,6 +94,10 @@ def lib():
         L.orc_merge_lse.restype = None
         L.orc_value_gate.argtypes = [P, P, P, P, P, P, i32, i32, i32, P, P]
         L.orc_value_gate.restype = None
+        L.orc_mxfp4_block.argtypes = [P, P]
+        L.orc_mxfp4_block.restype = None
+        L.orc_absorb_query.argtypes = [P, P, P, P, i32, i32, i32, f32, P, P]
+        L.orc_absorb_query.restype = None
         L.orc_bf16_round_array.argtypes = [P, P, i64]
         L.orc_bf16_round_array.restype = None
         L.orc_fp8_encode_array.argtypes = [P, P, i64]
@@ -256,6 +260,33 @@ def value_gate(latent, gate, lengths, qlen: int, w_bf16=None, w_fp4=None, w_scal
     lib().orc_value_gate(_p(latent), _p(w_bf16), _p(w_fp4), _p(w_scale), _p(gate), _p(lengths),
                          batch, qlen, H, _p(acc), _p(out))
     return acc, out
+
+
+def mxfp4_block(values) -> np.ndarray:
+    """One block of 32 values -> its MXFP4 quantisation, dequantised (f64)."""
+    v = _c(np.asarray(values, np.float64).reshape(32), np.float64)
+    out = np.empty(32, np.float64)
+    lib().orc_mxfp4_block(_p(v), _p(out))
+    return out
+
+
+def absorb_query(q_nope, q_pe, w_k, w_scale, fp8: bool = False, q_scale: float = 1.0):
+    """The absorbed query: q_nope [rows, H, 128] and q_pe [rows, H, 64] bf16
+    bits, W_K codes [H, 512, 64] u8 and scales [H, 512, 4] u8.  Returns (y f64
+    [rows, H, 512] exact products, out [rows, H, 576] bf16 bits or fp8 codes)."""
+    q_nope = _c(q_nope, np.uint16)
+    rows, heads, k = q_nope.shape
+    assert k == 128
+    q_pe = _c(q_pe, np.uint16)
+    assert q_pe.shape == (rows, heads, D_ROPE)
+    w_k = _c(w_k, np.uint8)
+    w_scale = _c(w_scale, np.uint8)
+    assert w_k.shape == (heads, D_LATENT, 64) and w_scale.shape == (heads, D_LATENT, 4)
+    y = np.empty((rows, heads, D_LATENT), np.float64)
+    out = np.empty((rows, heads, D_QK), np.uint8 if fp8 else np.uint16)
+    lib().orc_absorb_query(_p(q_nope), _p(q_pe), _p(w_k), _p(w_scale), rows, heads, 1 if fp8 else 0,
+                           float(q_scale), _p(out), _p(y))
+    return y, out
 
 
 def num_threads() -> int:

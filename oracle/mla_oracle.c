@@ -170,6 +170,109 @@ void orc_concat_quant_fp8(const uint16_t* ql_nope, const uint16_t* q_pe, float q
   }
 }
 
+/* ---------------------------------------- absorbed-query producer (W_UK) */
+
+/* The E2M1 magnitudes in code order (OCP MX v1.0): codes 0..7 are
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static double e2m1_magnitude(int code) { return orc_e2m1_decode((uint8_t)code); }
+
+/* MXFP4 quantisation of one block of 32 values, dequantised (OCP MX v1.0,
+ * conversion to an MX format): the shared exponent is
+ *   X = floor(log2(max_i |v_i|)) - 2   (2: the largest E2M1 exponent),
+ * held to the E8M0 range [-127, 127]; each element is v_i / 2^X rounded to
+ * the nearest E2M1 value (ties to the even code), values beyond the largest
+ * (6) taking 6.  out_i = (that value, with the sign of v_i) * 2^X.  Readings
+ * taken where the spec leaves it to the implementation: a block holding a
+ * NaN or an infinity dequantises to NaN; an all-zero block to zeros. */
+void orc_mxfp4_block(const double* v, double* out) {
+  double amax = 0.0;
+  int bad = 0;
+  for (int i = 0; i < 32; ++i) {
+    if (!isfinite(v[i])) bad = 1;
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  }
+  if (bad) {
+    for (int i = 0; i < 32; ++i) out[i] = NAN;
+    return;
+  }
+  if (amax == 0.0) {
+    for (int i = 0; i < 32; ++i) out[i] = 0.0;
+    return;
+  }
+  int e;
+  frexp(amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2(amax)) = e - 1 */
+  int X = (e - 1) - 2;
+  if (X < -127) X = -127;
+  if (X > 127) X = 127;
+  for (int i = 0; i < 32; ++i) {
+    double a = ldexp(fabs(v[i]), -X); /* exact: a power-of-two scaling */
+    int best = 0;
+    for (int c = 1; c < 8; ++c) {
+      double dc = fabs(a - e2m1_magnitude(c)), db = fabs(a - e2m1_magnitude(best));
+      if (dc < db || (dc == db && (c & 1) == 0)) best = c;
+    }
+    double q = ldexp(e2m1_magnitude(best), X);
+    out[i] = signbit(v[i]) ? -q : q;
+  }
+}
+
+/* The absorbed query of [MLA] `pre`: ql_nope = batched_gemm_a16wfp4(
+ * q_nope^T, W_K, W_K_scale, transpose_bm=True, prequant=True,
+ * y_scale=q_scale or None), then the concat with q_pe (and, on the fp8
+ * path, its quantisation).  Readings taken (the page shows the call, not
+ * what its flags compute):
+ *   - W_K of head h is a [512][128] MXFP4 matrix: row n holds 128 E2M1 codes
+ *     (two per byte, element 2k in the low nibble) and one E8M0 scale per 32
+ *     along k; y[t][h][n] = sum_k x[t][h][k] * W_K[h][n][k].
+ *   - transpose_bm: the per-head product [H][S][512] is laid out [S][H][512].
+ *   - prequant: the bf16 activation q_nope[t][h][:] is first quantised to
+ *     MXFP4 in blocks of 32 along k (orc_mxfp4_block), so both operands are
+ *     MXFP4; the product is computed exactly here.
+ *   - y_scale given (out_fp8 = 1): the product leaves as fp8 E4M3 codes
+ *     E(f32(y) / q_scale) (binary32 division, the encoder E of the cache
+ *     write) and the concat encodes q_pe the same way; absent (out_fp8 = 0),
+ *     y is rounded to bf16 and q_pe is copied.
+ * q_nope [rows][heads][128] and q_pe [rows][heads][64] are bf16 bits;
+ * w_k [heads][512][64] bytes, w_scale [heads][512][4]; out is
+ * [rows][heads][576] (bf16 bits or fp8 codes); y_out (nullable)
+ * [rows][heads][512] receives the exact products. */
+void orc_absorb_query(const uint16_t* q_nope, const uint16_t* q_pe, const uint8_t* w_k, const uint8_t* w_scale,
+                      int32_t rows, int32_t heads, int32_t out_fp8, float q_scale, void* out, double* y_out) {
+  int64_t n_th = (int64_t)rows * heads;
+#pragma omp parallel for schedule(static)
+  for (int64_t th = 0; th < n_th; ++th) {
+    int64_t h = th % heads;
+    double x[128], xq[128];
+    for (int k = 0; k < 128; ++k) x[k] = orc_bf16_decode(q_nope[th * 128 + k]);
+    for (int b = 0; b < 4; ++b) orc_mxfp4_block(x + 32 * b, xq + 32 * b);
+    for (int n = 0; n < ORC_D_LATENT; ++n) {
+      double y = 0.0;
+      for (int k = 0; k < 128; ++k) {
+        uint8_t byte = w_k[(h * ORC_D_LATENT + n) * 64 + k / 2];
+        uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+        double w = orc_e2m1_decode(nib) * orc_e8m0_decode(w_scale[(h * ORC_D_LATENT + n) * 4 + k / 32]);
+        y += xq[k] * w;
+      }
+      if (y_out) y_out[th * ORC_D_LATENT + n] = y;
+      if (out_fp8) {
+        float scaled = (float)y / q_scale; /* binary32 division */
+        ((uint8_t*)out)[th * ORC_D_QK + n] = orc_fp8_encode((double)scaled);
+      } else {
+        ((uint16_t*)out)[th * ORC_D_QK + n] = orc_bf16_round(y);
+      }
+    }
+    for (int c = 0; c < ORC_D_ROPE; ++c) {
+      uint16_t pe = q_pe[th * ORC_D_ROPE + c];
+      if (out_fp8) {
+        float scaled = (float)orc_bf16_decode(pe) / q_scale;
+        ((uint8_t*)out)[th * ORC_D_QK + ORC_D_LATENT + c] = orc_fp8_encode((double)scaled);
+      } else {
+        ((uint16_t*)out)[th * ORC_D_QK + ORC_D_LATENT + c] = pe;
+      }
+    }
+  }
+}
+
 /* ---------------------------------------------------------- split bounds */
 
 static int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -588,3 +588,137 @@ def test_concat_quant_closed_forms(oracle):
     assert np.array_equal(got[0, 0, :codes.size], codes)
     assert list(got[0, 0, 512:516]) == [0x7E, 0xFE, 0x7F, 0x7E]
     assert (got[0, 0, 516:] == 0).all()
+
+
+# ------------------------------------------- absorbed query (W_UK, MXFP4)
+
+def _e2m1_grid():
+    """E2M1 magnitudes by code, from the OCP MX table in tests/golden."""
+    table = {int(l.split()[0]): float(l.split()[1]) for l in open(os.path.join(GOLDEN, "ocp_mx_e2m1.txt"))
+             if l[0] != "#" and l.strip()}
+    return np.array([table[c] for c in range(8)])
+
+
+def test_mxfp4_block_is_the_nearest_grid_point(oracle):
+    # Every element is the E2M1 value nearest to v / 2^X (brute force over
+    # the table; a tie takes the even code), times 2^X, with the OCP shared
+    # exponent X = floor(log2(max |v|)) - 2 (frexp gives the exponent).
+    grid = _e2m1_grid()
+    rng = np.random.default_rng(41)
+    for it in range(300):
+        scale = 2.0 ** rng.integers(-20, 20)
+        v = rng.standard_normal(32) * scale
+        if it % 3 == 0:  # exact ties: midpoints of the grid at the block's exponent
+            amax_exp = int(np.frexp(np.abs(v).max())[1]) - 1
+            X = amax_exp - 2
+            mids = (grid[:-1] + grid[1:]) / 2
+            v[:7] = mids * 2.0 ** X * np.sign(rng.standard_normal(7))
+            v[7] = np.abs(v).max()  # keep the block maximum
+        out = oracle.mxfp4_block(v)
+        X = int(np.frexp(np.abs(v).max())[1]) - 1 - 2
+        a = np.abs(v) / 2.0 ** X
+        q = np.abs(out) / 2.0 ** X
+        for ai, qi in zip(a, q):
+            d = np.abs(grid - ai)
+            best = np.flatnonzero(d == d.min())
+            code = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert qi == grid[code], (ai, qi)
+        assert np.all((np.signbit(out) == np.signbit(v)) | (out == 0))
+
+
+def test_mxfp4_block_closed_forms(oracle):
+    # values on the grid of their block come back unchanged; the largest
+    # element beyond 6 * 2^X is clamped to 6 * 2^X; ties go to the even code
+    # (worked by hand from the OCP table: at X = 0, 0.25 -> 0, 0.75 -> 1,
+    # 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4); powers of two scale
+    # through; zero and non-finite blocks.
+    assert np.array_equal(oracle.mxfp4_block(np.ones(32)), np.ones(32))
+    on_grid = np.array([6, 4, 3, 2, 1.5, 1, 0.5, 0] * 4) * 2.0 ** -5
+    assert np.array_equal(oracle.mxfp4_block(on_grid), on_grid)
+    v = np.zeros(32)
+    v[0] = 7.0                      # max 7: X = 0, 7 -> 6
+    v[1:8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    want = np.zeros(32)
+    want[0:8] = [6, 0, 1, 1, 2, 2, 4, 4]
+    assert np.array_equal(oracle.mxfp4_block(v), want)
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal(32)
+    base = oracle.mxfp4_block(x)
+    for j in (-30, -3, 5, 40):
+        assert np.array_equal(oracle.mxfp4_block(x * 2.0 ** j), base * 2.0 ** j)
+    assert np.array_equal(oracle.mxfp4_block(-x), -base)
+    assert np.array_equal(oracle.mxfp4_block(np.zeros(32)), np.zeros(32))
+    bad = x.copy()
+    bad[3] = np.nan
+    assert np.isnan(oracle.mxfp4_block(bad)).all()
+    bad[3] = np.inf
+    assert np.isnan(oracle.mxfp4_block(bad)).all()
+    # a block below the E8M0 range: X is held at -127, so elements are
+    # multiples of 2^-128 (the smallest E2M1 step times 2^-127)
+    tiny = rng.standard_normal(32) * 2.0 ** -135
+    t = oracle.mxfp4_block(tiny)
+    assert np.all(np.abs(t / 2.0 ** -128 - np.round(t / 2.0 ** -128)) == 0) and np.abs(t).max() <= 6 * 2.0 ** -127
+
+
+def _absorb_inputs(rng, rows, heads, scale_lo=118, scale_hi=125):
+    qn = synth.to_bf16_bits(rng.standard_normal((rows, heads, 128)).astype(np.float32))
+    qp = synth.to_bf16_bits(rng.standard_normal((rows, heads, 64)).astype(np.float32))
+    wk = rng.integers(0, 256, (heads, 512, 64), dtype=np.uint8)
+    ws = rng.integers(scale_lo, scale_hi + 1, (heads, 512, 4)).astype(np.uint8)
+    return qn, qp, wk, ws
+
+
+def test_absorb_query_matches_matmul_on_table_expanded_weights(oracle):
+    # y = (MXFP4-quantised q_nope) @ W_K^T per head, with W_K expanded from
+    # the OCP E2M1 table and 2^(s-127): numpy einsum (library routine) on the
+    # block quantiser's output (pinned above); the bf16 output is y rounded,
+    # q_pe is copied bit for bit
+    rng = np.random.default_rng(43)
+    rows, heads = 5, 3
+    qn, qp, wk, ws = _absorb_inputs(rng, rows, heads)
+    y, out = oracle.absorb_query(qn, qp, wk, ws)
+    grid = _e2m1_grid()
+    mag = np.concatenate([grid, -grid])
+    W = mag[np.stack([wk & 0xF, wk >> 4], -1).reshape(heads, 512, 128)] * \
+        np.repeat(2.0 ** (ws.astype(np.float64) - 127), 32, axis=-1)
+    x = oracle.bf16_decode(qn)
+    xq = np.stack([oracle.mxfp4_block(x[t, h, 32 * b:32 * b + 32])
+                   for t in range(rows) for h in range(heads) for b in range(4)]).reshape(rows, heads, 128)
+    ref = np.einsum("thk,hnk->thn", xq, W)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=0)
+    assert np.array_equal(out[..., :512], oracle.bf16_round(y))
+    assert np.array_equal(out[..., 512:], qp)
+
+
+def test_absorb_query_fp8_matches_torch_cast_in_range(oracle):
+    # the fp8 path: E(f32(y) / q_scale) and E(q_pe / q_scale) are torch's
+    # float8_e4m3fn cast of the binary32 quotients (in range)
+    rng = np.random.default_rng(44)
+    qn, qp, wk, ws = _absorb_inputs(rng, 4, 2, 121, 125)
+    for q_scale in (1.0, 0.5, 3.0):
+        y, out = oracle.absorb_query(qn, qp, wk, ws, fp8=True, q_scale=q_scale)
+        yq = torch.from_numpy(y.astype(np.float32)) / torch.tensor(q_scale, dtype=torch.float32)
+        assert float(yq.abs().max()) < 448
+        ref = yq.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(out[..., :512], ref)
+        pe = torch.from_numpy(oracle.bf16_decode(qp).astype(np.float32)) / torch.tensor(q_scale, dtype=torch.float32)
+        assert np.array_equal(out[..., 512:], pe.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def test_absorb_query_identity_weights(oracle):
+    # W_K rows that pick one k (code 2 = 1.0 at k = n % 128, scale 2^0, all
+    # other codes 0): y[n] is the quantised q_nope element n % 128 itself
+    rng = np.random.default_rng(45)
+    rows, heads = 3, 2
+    qn, qp, _, _ = _absorb_inputs(rng, rows, heads)
+    wk = np.zeros((heads, 512, 64), np.uint8)
+    for n in range(512):
+        k = n % 128
+        wk[:, n, k // 2] = 2 << (4 * (k & 1))
+    ws = np.full((heads, 512, 4), 127, np.uint8)
+    y, _ = oracle.absorb_query(qn, qp, wk, ws)
+    x = oracle.bf16_decode(qn)
+    for t in range(rows):
+        for h in range(heads):
+            xq = np.concatenate([oracle.mxfp4_block(x[t, h, 32 * b:32 * b + 32]) for b in range(4)])
+            assert np.array_equal(y[t, h], np.tile(xq, 4))
