@@ -8,6 +8,8 @@
  * (classes `MlaValue`, `MlaGate`) describe it:
  *
  *   mla_kv_write        new tokens' [kv_c | k_pe] rows -> fp8 cache rows
+ *   mla_absorb_query    q_nope x W_UK (MXFP4) concatenated with q_pe -> the
+ *                       absorbed query rows (bf16, or fp8 with q_scale)
  *   mla_concat_quant_fp8  absorbed query [ql_nope | q_pe] -> fp8 query rows
  *   mla_decode_partial  absorbed queries attend over the paged fp8 cache:
  *                       split-KV partials o (bf16) and LSE (f32)
@@ -85,6 +87,45 @@ const char* mla_status_string(int status);
 int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
                  int64_t k_pe_stride, const int64_t* slot_mapping, int32_t n, uint8_t* kv_cache,
                  int64_t num_slots, float kv_scale, void* stream);
+
+/*
+ * The absorbed query ([MLA] `pre`: ql_nope = batched_gemm_a16wfp4(q_nope^T,
+ * W_K, W_K_scale, transpose_bm, prequant, y_scale), then the concat with q_pe
+ * and, on the fp8 path, the quantisation).  For row t < rows, head h < heads:
+ *   xq = q_nope[t][h][0:128] quantised to MXFP4 in blocks of 32 (OCP MX:
+ *        shared exponent X = floor(log2 max|v|) - 2 held to [-127, 127], each
+ *        v / 2^X rounded to the nearest E2M1 value with ties to the even code,
+ *        past 6 clamped to 6; a block holding NaN or inf gives NaN),
+ *   y[n] = sum_k xq[k] * W_K[h][n][k]   (n < 512, W_K decoded exactly;
+ *        products exact, sums in binary32),
+ *   out_fp8 = 0:  out[t][h][0:512] = bf16(y),  out[t][h][512:576] = q_pe[t][h]
+ *   out_fp8 = 1:  out[t][h][0:512] = E(y / q_scale),
+ *                 out[t][h][512:576] = E(q_pe[t][h] / q_scale)
+ * (correctly rounded binary32 divisions, E the encoder of mla_kv_write), so
+ * the fp8 rows are the q8 of mla_decode_partial_fp8q with this q_scale.
+ *   q_nope   [rows][heads][128] bf16, strides (qn_row, qn_head)
+ *   q_pe     [rows][heads][64] bf16, strides (qp_row, qp_head) (e.g. the two
+ *            slices of a [rows][heads][192] projection output); strides
+ *            multiples of 8, both 16-byte aligned
+ *   w_k      [heads][512][64] u8: row n of head h holds 128 E2M1 codes, two
+ *            per byte, element 2j in the low nibble; strides (wk_head, wk_n)
+ *            in bytes
+ *   wk_scale [heads][512][4] u8 E8M0 (2^(s-127); 0xFF NaN), one per 32 along
+ *            k; strides (wks_head, wks_n) in bytes; strides of w_k and
+ *            wk_scale multiples of 4, both 4-byte aligned
+ *   out      [rows][heads][576] bf16 (out_fp8 = 0) or u8 codes (out_fp8 = 1),
+ *            strides (out_row, out_head) in its elements, multiples of 8
+ *            (bf16) or 16 (fp8), 16-byte aligned (e.g. the query buffer of
+ *            mla_decode_partial with padded heads)
+ * Errors: MLA_ERR_INVALID for rows < 0, heads < 1, out_fp8 not 0 or 1, a null
+ * pointer, or (out_fp8 = 1) q_scale not > 0 and finite; MLA_ERR_UNSUPPORTED
+ * for the alignment rules above or heads > 65535.  rows = 0 is a no-op.
+ */
+int mla_absorb_query(const uint16_t* q_nope, int64_t qn_row, int64_t qn_head, const uint16_t* q_pe,
+                     int64_t qp_row, int64_t qp_head, const uint8_t* w_k, int64_t wk_head, int64_t wk_n,
+                     const uint8_t* wk_scale, int64_t wks_head, int64_t wks_n, int32_t rows, int32_t heads,
+                     int32_t out_fp8, float q_scale, void* out, int64_t out_row, int64_t out_head,
+                     void* stream);
 
 /*
  * The fp8 query ([MLA] `pre`: _decode_concat_quant_fp8_op(ql_nope, q_pe,

@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
                                                        f32, i32, i32, i32, P, i64, i64, i64, P, i64, i64,
                                                        i64, P, P]
         L.mla_concat_quant_fp8.argtypes = [P, i64, i64, P, i64, i64, f32, i32, i32, P, i64, i64, P]
+        L.mla_absorb_query.argtypes = [P, i64, i64, P, i64, i64, P, i64, i64, P, i64, i64, i32, i32, i32, f32, P,
+                                       i64, i64, P]
         L.mla_decode_partial_fp8q.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32, f32,
                                               i32, i32, i32, P, i64, i64, i64, P, i64, i64, i64, P]
         L.mla_merge_value_gate.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, P, i64, i64, P, i64,
@@ -60,7 +62,7 @@ def lib() -> ctypes.CDLL:
                                     i64, i64, P]
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
-        for name in ("mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
+        for name in ("mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
                      "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -102,6 +104,30 @@ def kv_write(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
                             _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0], float(kv_scale),
                             _stream())
     _check(st, "mla_kv_write")
+
+
+def absorb_query(q_nope: torch.Tensor, q_pe: torch.Tensor, w_k: torch.Tensor, w_k_scale: torch.Tensor,
+                 out: torch.Tensor, q_scale: float | None = None) -> None:
+    """The absorbed query rows out [rows, >=H, 576] = [q_nope x W_UK | q_pe]:
+    bf16 out (q_scale None) or fp8 codes E(. / q_scale) (uint8 or
+    float8_e4m3fn out).  q_nope [rows, H, 128] and q_pe [rows, H, 64] bf16
+    (strided views allowed); W_UK as MXFP4 codes w_k [H, 512, 64] u8 and
+    E8M0 scales w_k_scale [H, 512, 4] u8."""
+    rows, heads = q_nope.shape[0], q_nope.shape[1]
+    if q_nope.shape[-1] != 128 or tuple(q_pe.shape) != (rows, heads, D_ROPE):
+        raise MlaError("q_nope must be [rows, H, 128] and q_pe [rows, H, 64]")
+    if tuple(w_k.shape) != (heads, D_LATENT, 64) or tuple(w_k_scale.shape) != (heads, D_LATENT, 4):
+        raise MlaError("w_k must be [H, 512, 64] and w_k_scale [H, 512, 4]")
+    if out.shape[0] != rows or out.shape[1] < heads or out.shape[2] != D_QK:
+        raise MlaError("out must be [rows, >=H, 576]")
+    fp8 = q_scale is not None
+    st = lib().mla_absorb_query(
+        _dev(q_nope, "q_nope", _BF16), q_nope.stride(0), q_nope.stride(1), _dev(q_pe, "q_pe", _BF16),
+        q_pe.stride(0), q_pe.stride(1), _dev(w_k, "w_k", (torch.uint8,)), w_k.stride(0), w_k.stride(1),
+        _dev(w_k_scale, "w_k_scale", (torch.uint8,)), w_k_scale.stride(0), w_k_scale.stride(1), rows, heads,
+        1 if fp8 else 0, float(q_scale) if fp8 else 1.0, _dev(out, "out", _U8 if fp8 else _BF16), out.stride(0),
+        out.stride(1), _stream())
+    _check(st, "mla_absorb_query")
 
 
 def concat_quant_fp8(ql_nope: torch.Tensor, q_pe: torch.Tensor, q_scale: float, q8: torch.Tensor) -> None:

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_fp8.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["kv_write.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip", "merge_value.hip"]
+SOURCES = ["kv_write.hip", "absorb_q.hip", "decode_partial.hip", "merge_lse.hip", "value_gate.hip",
+           "merge_value.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -6,32 +6,6 @@
 
 namespace mla {
 
-// binary32 -> fp8 E4M3 (OCP fn): round to nearest even, saturate to +-448,
-// NaN -> 0x7F.
-__device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float v) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t sign = (u >> 24) & 0x80u;
-  uint32_t a = u & 0x7FFFFFFFu;
-  if (a > 0x7F800000u) return 0x7Fu;
-  float av = __uint_as_float(a);
-  uint32_t code;
-  if (av < 0.015625f) {
-    // subnormal range: quantum 2^-9; rint rounds ties to even; 8 -> 0x08 (2^-6)
-    code = (uint32_t)__builtin_rintf(av * 512.0f);
-  } else {
-    // keep 3 mantissa bits, nearest even (carry may bump the exponent)
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    int e = (int)(r >> 23) - 127 + 7;
-    uint32_t m = (r >> 20) & 7u;
-    if (e > 15 || (e == 15 && m == 7)) {
-      code = 0x7Eu;  // saturate (448)
-    } else {
-      code = ((uint32_t)e << 3) | m;
-    }
-  }
-  return code | sign;
-}
-
 // One thread per 8 consecutive columns of one token: 72 threads per row.
 __global__ void __launch_bounds__(256) kv_write_kernel(const uint16_t* __restrict__ kv_c,
                                                        int64_t kv_c_stride,

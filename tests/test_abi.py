@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_path():
     names = declared_functions()
-    for n in ["mla_kv_write", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
+    for n in ["mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
               "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate", "mla_split_plan", "mla_status_string"]:
         assert n in names
 
@@ -212,3 +212,25 @@ def test_hostplan_partition_runs_on_the_host(mlib):
         assert L.mla_decode_partial_hostplan(fake, 576, 576, 2, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2, nw, 1,
                                              fake, 0, 0, 0, fake, 0, 0, 0, bad.ctypes.data_as(ctypes.c_void_p),
                                              null) == 1
+
+
+def test_absorb_query_argument_errors(mlib):
+    L = mlib.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every case is rejected (or a no-op) on the host
+
+    def call(rows=4, heads=2, fp8=0, qs=1.0, qn=fake, qn_row=256, wk_n=64, out_row=1152, out=fake):
+        return L.mla_absorb_query(qn, qn_row, 128, fake, 128, 64, fake, 512 * 64, wk_n, fake, 512 * 4, 4, rows,
+                                  heads, fp8, qs, out, out_row, 576, null)
+
+    assert call(rows=0) == 0                   # no rows: a no-op
+    assert call(rows=-1) == 1
+    assert call(heads=0) == 1
+    assert call(fp8=2) == 1                    # unknown output format
+    assert call(qn=null) == 1
+    assert call(out=null) == 1
+    assert call(fp8=1, qs=0.0) == 1            # the fp8 path needs q_scale > 0 and finite
+    assert call(fp8=1, qs=float("inf")) == 1
+    assert call(qn_row=260) == 2               # bf16 rows in 16-byte chunks
+    assert call(wk_n=66) == 2                  # W_K code words are 4-byte aligned
+    assert call(fp8=1, out_row=1160) == 2      # fp8 output rows in 16-byte chunks

@@ -659,6 +659,92 @@ def test_value_gate_mxfp4_edge_scales(ops, oracle):
         assert np.abs(g[:, h][fin] - r[:, h][fin]).max() <= OUT_REL_TOL * scale, h
 
 
+# ------------------------------------------------ absorbed query (W_UK)
+
+def _ulp_far(x, margin, mant_bits, emin):
+    """True where x lies farther than `margin` from a rounding midpoint of a
+    binary format with `mant_bits` fraction bits and least exponent emin."""
+    mag = np.abs(x)
+    e = np.floor(np.log2(np.maximum(mag, 1e-300)))
+    ulp = 2.0 ** (np.maximum(e, emin) - mant_bits)
+    frac = mag / ulp - np.floor(mag / ulp)
+    return np.abs(frac - 0.5) * ulp > margin, ulp
+
+
+@pytest.mark.parametrize("rows,heads,fp8,q_scale", [(5, 3, False, None), (37, 12, True, 0.5), (256, 96, False, None),
+                                                    (256, 96, True, 1.0 / 16), (16, 1, True, 2.0)])
+def test_absorb_query_parity(ops, oracle, rows, heads, fp8, q_scale):
+    """mla_absorb_query against the oracle: q_nope and q_pe are strided
+    slices of one [rows, heads, 192] projection output, the result goes into
+    a query buffer with 4 pad heads (left untouched).  Blocks with a NaN,
+    all zeros, values below the binary32 normal range and exact E2M1 ties
+    are included.  The rope part is bit-exact; each product is compared bit
+    for bit (bf16, or the fp8 code) where the exact value lies farther from a
+    rounding midpoint than a binary32 sum of 128 exact products can move it
+    (2^-18 of the sum of |terms|), within one unit elsewhere."""
+    from mla_latent_kv_fp8_amd.synth import to_bf16_bits
+
+    _announce(f"absorb_query rows={rows} heads={heads} fp8={fp8}")
+    rng = np.random.default_rng(rows * 7 + heads)
+    proj = rng.standard_normal((rows, heads, 192)).astype(np.float32)
+    proj[0, 0, 5] = np.nan                          # a NaN block: its row's products are NaN
+    proj[rows - 1, heads - 1, 32:64] = 0.0          # an all-zero block
+    proj[rows // 2, 0, 64:96] *= 2.0 ** -130        # values below the binary32 normal range
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    mids = (grid[:-1] + grid[1:]) / 2
+    proj[min(1, rows - 1), heads // 2, 96:103] = mids * 0.25   # exact ties at X = -2
+    proj[min(1, rows - 1), heads // 2, 103] = 1.5              # the block maximum: X = -2
+    pb = to_bf16_bits(proj)
+    wk = rng.integers(0, 256, (heads, 512, 64), dtype=np.uint8)
+    ws = rng.integers(119, 126, (heads, 512, 4)).astype(np.uint8)
+    qn, qp = pb[..., :128], pb[..., 128:]
+    y, ref = oracle.absorb_query(qn, qp, wk, ws, fp8=fp8, q_scale=q_scale if fp8 else 1.0)
+    hp = heads + 4
+    pd = _bf16_dev(pb)
+    if fp8:
+        out = torch.full((rows, hp, 576), 0x5A, dtype=torch.uint8, device="cuda")
+    else:
+        out = torch.full((rows, hp, 576), 1234.0, dtype=torch.bfloat16, device="cuda")
+    ops.absorb_query(pd[..., :128], pd[..., 128:], torch.from_numpy(wk).cuda(), torch.from_numpy(ws).cuda(), out,
+                     q_scale=q_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy() if fp8 else _np_bf16(out)
+    pad = got[:, heads:]
+    assert (pad == (0x5A if fp8 else to_bf16_bits(np.float32(1234.0)))).all()
+    got = got[:, :heads]
+    assert np.array_equal(got[..., 512:], ref[..., 512:])            # rope part: bit-exact
+    # sum of |terms| per product, from the oracle's quantised rows and the
+    # table-expanded weights
+    mag = np.concatenate([grid, -grid])
+    W = mag[np.stack([wk & 0xF, wk >> 4], -1).reshape(heads, 512, 128)] * \
+        np.repeat(2.0 ** (ws.astype(np.float64) - 127), 32, axis=-1)
+    x = oracle.bf16_decode(qn)
+    xq = np.stack([oracle.mxfp4_block(x[t, h, 32 * b:32 * b + 32])
+                   for t in range(rows) for h in range(heads) for b in range(4)]).reshape(rows, heads, 128)
+    nan_th = np.isnan(xq).any(-1)
+    xq = np.nan_to_num(xq)
+    abs_terms = np.einsum("thk,hnk->thn", np.abs(xq), np.abs(W))
+    margin = 2.0 ** -18 * abs_terms
+    g, r = got[..., :512], ref[..., :512]
+    if fp8:
+        assert (g[nan_th] == 0x7F).all() and (r[nan_th] == 0x7F).all()
+        v = y.astype(np.float32).astype(np.float64) / q_scale
+        far, _ = _ulp_far(v, margin / q_scale, 3, -6)
+        keep = ~nan_th[..., None] & np.ones_like(far)
+        assert np.array_equal(g[keep & far], r[keep & far])
+        gd, rd = oracle.fp8_decode(g[keep & ~far]), oracle.fp8_decode(r[keep & ~far])
+        _, ulp = _ulp_far(rd, 0, 3, -6)
+        assert np.all(np.abs(gd - rd) <= ulp * 1.0000001)
+    else:
+        assert np.isnan(oracle.bf16_decode(g[nan_th])).all()
+        far, ulp = _ulp_far(y, margin, 7, -126)
+        keep = ~nan_th[..., None] & np.ones_like(far)
+        assert far[keep].mean() > 0.5
+        assert np.array_equal(g[keep & far], r[keep & far])
+        assert np.all(np.abs(oracle.bf16_decode(g[keep & ~far]) - oracle.bf16_decode(r[keep & ~far]))
+                      <= ulp[keep & ~far] * 1.0000001)
+
+
 # ------------------------------------------- fused merge + value + gate
 
 @pytest.mark.parametrize("fmt,ns,rows,qlen,heads", [("bf16", 16, 64, 1, 96), ("bf16", 3, 13, 1, 5),
