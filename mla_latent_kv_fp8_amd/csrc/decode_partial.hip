@@ -17,17 +17,18 @@
 //    tiles are issued as soon as the indices have landed.
 //  * QK on 16x16x32 bf16 MFMAs as S^T = K . Q^T: A = 16 tokens x 32 dims of
 //    the staged tile (fp8 -> bf16 in registers), B = Q^T, loaded once per
-//    piece into accumulation registers (the 48-row block keeps the last
-//    256 dims in LDS instead, so that O and Q fit the register file).  Wave
+//    piece into accumulation registers (the 48-row block too: its whole
+//    query, 216 registers, with O in 96 arch registers).  Wave
 //    w owns token quarter w of every tile for all row groups, so each staged
 //    byte is converted to bf16 once per block.
-//  * Softmax: base-2, against a lazy per-row reference shared by the four
-//    waves: P = 2^(s*c - ref) in bf16, sums in f32.  One barrier per tile:
-//    each wave computes P optimistically and flags scores above its row's
-//    threshold (reference + 64); the flags travel with P^T and are read
-//    after the barrier.  A flagged tile (a piece's first, in practice)
-//    exchanges the quarter maxima; a row that outgrew its reference by more
-//    than 2^64 restarts the piece with the new one, so O is never rescaled.
+//  * Softmax: base-2, P = 2^(s*c - ref) in bf16, sums in f32, with a
+//    per-row reference ref that starts at 0.  Each lane keeps the running
+//    maximum of its scores; at the end of a piece the four quarters' row
+//    maxima are exchanged with the row sums, and a row whose maximum lies
+//    more than 64 log2 units from its reference takes the maximum as its
+//    reference and the piece runs again (P <= 2^64 then bounds bf16 P and
+//    the f32 sums).  No tile waits for a decision about the reference, and
+//    O is never rescaled.  One barrier per tile publishes P^T.
 //  * PV as O^T = V^T . P^T: wave w owns latent columns [128w, 128w+128).
 //    The A operand (8 tokens of one column) comes straight from the
 //    staged tile with ds_read_b64_tr_b8; the B operand is P^T, written to
@@ -570,7 +571,6 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
-  __shared__ __attribute__((aligned(16))) int32_t redflag[8];          // reference flags, by tile parity
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
@@ -842,20 +842,23 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
 
 
     f32x4 O[8][NRG];
-    // per row: reference (log2 units), raw-score threshold of the flag, -ref
-    float mref[NRG], thr[NRG], nmb[NRG], lsum[NRG];
-    const float inv_c = 1.0f / p.c_log2;
+    // per row: the softmax reference (log2 units) and its negation, the
+    // lane's share of the row sum, and the lane's running maximum score
+    // (raw score units)
+    float mref[NRG], nmb[NRG], lsum[NRG], rmax[NRG];
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
-      mref[g] = -INFINITY;
-      thr[g] = -INFINITY;
+      mref[g] = 0.0f;
       nmb[g] = 0.0f;
     }
 
-    // The piece runs more than once only when a row's score outgrew its
-    // reference by more than 2^64: the reference then moves up and the
-    // piece restarts from its first token (O is never rescaled, so the hot
-    // loop touches O only through the MFMAs).
+    // Every row starts with reference 0: P = 2^(s*c - ref) stays within
+    // 2^(+-64) of the row's largest term unless the row's maximum lies more
+    // than 64 log2 units away from the reference.  Whether it does is known
+    // at the end of the piece, from the exchanged row maxima: such a row
+    // takes its maximum as the reference and the piece runs again from its
+    // first token (once: the maxima do not change).  O is never rescaled,
+    // and no tile waits for a decision about the reference.
     bool again = true;
     bool restaged = false;  // the first segment's indices must be staged again
     while (again) {
@@ -865,9 +868,12 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
 #pragma unroll
       for (int g = 0; g < NRG; ++g) O[d][g] = f32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int g = 0; g < NRG; ++g) lsum[g] = 0.0f;
+    for (int g = 0; g < NRG; ++g) {
+      lsum[g] = 0.0f;
+      rmax[g] = -INFINITY;
+    }
 
-    for (int s0 = a; s0 < b && !again; s0 += IDX_CAP) {
+    for (int s0 = a; s0 < b; s0 += IDX_CAP) {
       const int slen = min(IDX_CAP, b - s0);
       const bool first_seg = s0 == a && !restaged;  // staged and issued with the query
       if (!first_seg) {
@@ -891,13 +897,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         __syncthreads();
       }
 
-      // One barrier per tile.  Each wave computes its quarter's scores and
-      // P against the shared reference optimistically and flags the rows
-      // that need a new one: a row's first finite maximum (its reference is
-      // set), or a maximum that outgrew the reference by more than 2^64
-      // (rare: the piece restarts with the new reference).  The decisions
-      // are block-uniform after the barrier, since every wave reads the same
-      // flags and the same exchanged maxima.
+      // One barrier per tile: it publishes P^T of tile it and tile it+1.
       for (int it = 0; it < ntiles; ++it) {
         const int t0 = s0 + NT * it;
         const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
@@ -926,64 +926,51 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
               }
           }
         }
-        // ---- flag: a score of this quarter above its row's threshold (the
-        // reference plus 2^64, or any finite score while there is none)
-        bool need = false;
+        // ---- the running maxima (a NaN score leaves them; it poisons the sum)
 #pragma unroll
         for (int g = 0; g < NRG; ++g)
-          need |= fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3])) > thr[g];
-        // (the vote runs on all lanes, outside the single-lane store)
-        const bool any_need = __any(need);
-        if (lane == 0) redflag[4 * (it & 1) + wave] = any_need ? 1 : 0;
+          rmax[g] = fmaxf(rmax[g], fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3])));
         float ps[NRG];
         p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
         i32x2 v0[8];
         read_v(kt, 0, vo, v0);               // in flight across the barrier
         if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
-        __syncthreads();                     // P^T and flags of tile it; tile it+1 visible
-        const i32x4 f4 = *(const MLA_LDS i32x4*)&redflag[4 * (it & 1)];
+        __syncthreads();                     // P^T of tile it; tile it+1 visible
         if (it + 2 < ntiles)
           issue_tile(p.kv, p.num_slots, nrow, safe_row, kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
-        if (__builtin_amdgcn_readfirstlane(f4[0] | f4[1] | f4[2] | f4[3])) {
-          // ---- rare (a piece's first tile): exchange the quarter maxima;
-          // rows without a reference take theirs, rows that outgrew theirs
-          // by more than 2^64 restart the piece with the new one
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) {
-            const float lm = group_max4(fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3]))) * p.c_log2;
-            if (lg == 0) redmax[(16 * g + lr) * 4 + wave] = lm;
-          }
-          __syncthreads();
-          bool grow = false;
-#pragma unroll
-          for (int g = 0; g < NRG; ++g) {
-            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
-            const float mnew = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
-            if (mref[g] == -INFINITY) {
-              mref[g] = mnew;  // stays -inf while the row has seen no finite score
-            } else if (mnew > mref[g] + kLazy) {
-              mref[g] = mnew;
-              grow = true;
-            }
-            thr[g] = mref[g] == -INFINITY ? -INFINITY : (mref[g] + kLazy) * inv_c;
-            nmb[g] = mref[g] == -INFINITY ? 0.0f : -mref[g];
-          }
-          if (__any(grow)) {  // the same maxima in every wave: block-uniform
-            again = true;
-            break;
-          }
-          p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
-          __syncthreads();  // the recomputed P^T is complete
-        }
 #pragma unroll
         for (int g = 0; g < NRG; ++g) lsum[g] += ps[g];
         pv_tile<NRG>(kt, ptb, O, v0, vo, lane);
       }
-      if (again) {
-        wait_vm_all();  // tile loads still in flight land before anything is restaged
-        __syncthreads();
-        restaged = true;
+    }
+    // ---- end of the piece: the row sums and maxima of the four quarters;
+    // rows whose maximum lies more than 64 log2 units from their reference
+    // take it as the new reference and the piece runs again (a block-uniform
+    // decision: every wave reads the same maxima)
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      const float l = group_sum4(lsum[g]);
+      const float lm = group_max4(rmax[g]) * p.c_log2;
+      if (lg == 0) {
+        redsum[(16 * g + lr) * 4 + wave] = l;
+        redmax[(16 * g + lr) * 4 + wave] = lm;
       }
+    }
+    __syncthreads();
+    bool moved = false;
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      const f32x4 q4 = *reinterpret_cast<const f32x4*>(&redmax[(16 * g + lr) * 4]);
+      const float mx = fmaxf(fmaxf(q4[0], q4[1]), fmaxf(q4[2], q4[3]));
+      if (mx > mref[g] + kLazy || (mx != -INFINITY && mx < mref[g] - kLazy)) {
+        mref[g] = mx;
+        nmb[g] = -mx;
+        moved = true;
+      }
+    }
+    if (__any(moved)) {
+      again = true;
+      restaged = true;
     }
     }  // while (again)
 
@@ -991,12 +978,6 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // The row sums; O normalised to bf16 into LDS (every wave is past its
     // last PV after the first barrier, so the tile buffers are free), then
     // written out one whole 1 KB row per store instruction.
-#pragma unroll
-    for (int g = 0; g < NRG; ++g) {
-      const float l = group_sum4(lsum[g]);
-      if (lg == 0) redsum[(16 * g + lr) * 4 + wave] = l;
-    }
-    __syncthreads();
     MLA_LDS uint16_t* ost = (MLA_LDS uint16_t*)kbuf;
     uint64_t wmask = 0;  // block rows to write (a finite or NaN sum, row < M)
 #pragma unroll
