@@ -141,6 +141,13 @@ __device__ __forceinline__ void lds_dma4(const int32_t* gsrc, uint32_t lds_base)
 }
 #pragma clang diagnostic pop
 
+// floor(x / c) for x >= 0, c > 0: one 32-bit division when both fit (the
+// stream positions of up to 2^32 tokens), the 64-bit one otherwise
+__device__ __forceinline__ int64_t div_pos(int64_t x, int64_t c) {
+  if ((((uint64_t)x | (uint64_t)c) >> 32) == 0) return (int64_t)((uint32_t)x / (uint32_t)c);
+  return x / c;
+}
+
 __device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Issue the direct global->LDS loads of one 64-token tile.  Wave w loads the
@@ -166,30 +173,6 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots,
 
 constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
 constexpr int NBUF = 3;        // staged tiles in flight (triple buffering)
-// K-steps by which QK reads the query's LDS part ahead of its MFMAs: with one
-// wave per SIMD the LDS returns data only as fast as reads are in flight, and
-// two steps of reads (24 more VGPRs than one) keep more of them in flight
-#ifndef MLA_QLDS_AHEAD
-#define MLA_QLDS_AHEAD 2
-#endif
-#ifndef QREG3
-#define QREG3 5
-#endif
-#ifndef QPIN3
-#define QPIN3 9
-#endif
-// K-step pairs (64 dims each) of a bf16 query block staged in the staging
-// area (tile buffer 2); the 48-row block's other pairs are staged in the
-// query area of LDS at the same time, since 48 rows do not fit one buffer
-template <int NRG> constexpr int qstage_pairs() { return NRG >= 3 ? QREG3 : 9; }
-#ifndef MLA_QALL
-#define MLA_QALL 1
-#endif
-// K-step pairs of the query held in registers for the whole piece: all of
-// them, read once per piece from the two staging areas (with MLA_QALL 0 the
-// 48-row block instead reads the pairs past qstage_pairs from LDS every tile)
-template <int NRG> constexpr int qreg_pairs() { return MLA_QALL ? 9 : qstage_pairs<NRG>(); }
-
 // max over the 4 lane groups {l, l^16, l^32, l^48} with VALU lane swaps
 __device__ __forceinline__ float group_max4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -238,106 +221,70 @@ __device__ __forceinline__ void stage_idx(const int32_t* src, int n, MLA_LDS int
   }
 }
 
-// Query rows of one block plus the first index segment, all by direct
-// global->LDS loads.  With QR = qreg_pairs<NRG>(), dims [0, 64 QR) of row i
-// go to the staging area at qreg + i*qpitch_reg (read once into registers)
-// and dims [64 QR, 576) to the piece-resident area qlds + i*qpitch_lds
-// (layout below).  The register part takes 8 chunks of 16 B per 64 dims
-// plus one chunk of padding (which staggers the rows over the LDS banks)
-// where the block still fits the one tile buffer it is staged in.
-template <int NRG> constexpr int qw_reg() {
-  return 16 * NRG * (8 * qstage_pairs<NRG>() + 1) <= TILE_BYTES / 16 ? 8 * qstage_pairs<NRG>() + 1
-                                                                       : 8 * qstage_pairs<NRG>();
+// Query staging.  A block's query reaches LDS by direct loads in fragment
+// order: for a bf16 query, 1 KB block (g, s) holds at 16*lane the fragment
+// of K-step s = 2pp + h that lane (lr, lg) reads, dims 64pp + 16lg + 8h ..
+// +7 of row 16g + lr; an fp8 query takes one block per (g, pp), with dims
+// 64pp + 16lg .. +15 (both K-steps of the pair).  Each lane's row offsets
+// are computed once, so a load costs one address add, and the reads into
+// registers are contiguous.  Blocks 0..35 go to tile buffer 2, the rest to
+// the query area.
+template <int NRG, bool QF8> constexpr int q_blocks() { return (QF8 ? 9 : 18) * NRG; }
+template <int NRG, bool QF8> constexpr int q_area_bytes() {
+  return q_blocks<NRG, QF8>() * 1024 > TILE_BYTES ? q_blocks<NRG, QF8>() * 1024 - TILE_BYTES : 16;
 }
-template <int NRG> constexpr int qpitch_reg() { return 16 * qw_reg<NRG>(); }
-// The LDS part holds, per row, 8 chunks per K-step pair in the order the
-// QK reads them (chunk 4h + lg of a pair: dims 16lg + 8h .. +7 of it, so
-// one read instruction covers 64 contiguous bytes of each row), plus two
-// chunks of padding: a 544-byte pitch (48 rows) has no bank conflicts.
-template <int NRG> constexpr int qpitch_lds() { return 16 * (8 * (9 - qstage_pairs<NRG>()) + 2); }
-
-// An fp8 query block is staged whole, as its natural rows of 576 bytes
-// (36 chunks of 16 B) at qreg + 576 i; decode_q8 turns it into bf16 once per
-// piece.
-constexpr int Q8_PITCH = MLA_D_QK;
-
+__device__ __forceinline__ MLA_LDS uint8_t* q_block(MLA_LDS uint8_t* buf2, MLA_LDS uint8_t* qarea, int j) {
+  return j < TILE_BYTES / 1024 ? buf2 + 1024 * j : qarea + 1024 * (j - TILE_BYTES / 1024);
+}
+// The first segment's cache indices, then this wave's share of the query
+// blocks, all by direct global->LDS loads; returns how many of this wave's
+// loads are the query's (the caller waits for the indices alone first).
+// rowq[g]: offset of this lane's row (g, lr) in the query (elements).
 template <int NRG, bool QF8>
-__device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, int r, int m_lo, const int32_t* idx_src,
-                                               int nidx, MLA_LDS uint8_t* qreg, MLA_LDS uint8_t* qlds,
-                                               MLA_LDS int32_t* idx_lds, int wave, int lane) {
-  constexpr int RB = 16 * NRG;
-  constexpr int QR = qstage_pairs<NRG>();
+__device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, const int64_t (&rowq)[NRG],
+                                               const int32_t* idx_src, int nidx, MLA_LDS uint8_t* buf2,
+                                               MLA_LDS uint8_t* qarea, MLA_LDS int32_t* idx_lds, int wave,
+                                               int lane) {
+  constexpr int NT_G = QF8 ? 9 : 18;  // blocks per row group
+  const int lg = lane >> 4;
   // the indices go first: the caller waits for them alone and issues the
   // first tiles while the query is still in flight
   stage_idx(idx_src, nidx, idx_lds, wave, lane);
-  if constexpr (QF8) {
-    constexpr int NC = RB * (Q8_PITCH / 16);
-    constexpr int NR = (NC + 63) / 64;
-    static_assert(NR * 1024 <= TILE_BYTES, "an fp8 query block is staged in one tile buffer");
-    const uint8_t* q8_base =
-        p.q8 + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
+  int n = 0;
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) {
+    const uint8_t* base = QF8 ? p.q8 + rowq[g] + 16 * lg
+                              : reinterpret_cast<const uint8_t*>(p.q + rowq[g] + 16 * lg);
 #pragma unroll 1
-    for (int j0 = 0; j0 < NR; j0 += 4) {
-      const int j = j0 + wave;
-      if (j < NR) {
-        const int c = 64 * j + lane;
-        const int row = c / (Q8_PITCH / 16), part = c - (Q8_PITCH / 16) * row;
-        const int m = m_lo + row;
-        const uint8_t* g = q8_base;  // rows past the block or past M: the block's first row
-        if (row < RB && m < p.M) {
-          const int jj = m / p.heads, h = m - p.heads * jj;
-          g = p.q8 + (int64_t)(r * p.qlen + jj) * p.q_sr + (int64_t)h * p.q_sh + 16 * part;
-        }
-        lds_dma16(g, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qreg + 1024 * j)));
-      }
-    }
-    return (NR - wave + 3) / 4;
-  }
-  const uint16_t* q_base = p.q + (int64_t)(r * p.qlen + m_lo / p.heads) * p.q_sr + (int64_t)(m_lo % p.heads) * p.q_sh;
-  auto src_of = [&](int row, int dim8) -> const uint16_t* {
-    const int m = m_lo + row;
-    if (row >= RB || m >= p.M) return q_base;  // dummy: the block's first row
-    const int jj = m / p.heads, h = m - p.heads * jj;
-    return p.q + (int64_t)(r * p.qlen + jj) * p.q_sr + (int64_t)h * p.q_sh + dim8;
-  };
-  int nq = 0;
-  // part 0: register dims
-  {
-    constexpr int W = qw_reg<NRG>();
-    constexpr int NR = (RB * W + 63) / 64;
-    static_assert(NR * 1024 <= TILE_BYTES, "the register part is staged in one tile buffer");
-    nq += (NR - wave + 3) / 4;
-#pragma unroll 1
-    for (int j0 = 0; j0 < NR; j0 += 4) {
-      const int j = j0 + wave;
-      if (j < NR) {
-        const int c = 64 * j + lane;
-        const int row = c / W, part = c - W * (c / W);
-        const uint16_t* g = part < 8 * QR ? src_of(row, 8 * part) : q_base;
-        lds_dma16(reinterpret_cast<const uint8_t*>(g),
-                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qreg + 1024 * j)));
-      }
+    for (int t = wave; t < NT_G; t += 4) {
+      // bf16: K-step t = 2pp + h at dims 64pp + 8h (bytes 128pp + 16h); fp8: pair t at byte 64t
+      const int off = QF8 ? 64 * t : 128 * (t >> 1) + 16 * (t & 1);
+      lds_dma16(base + off, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)q_block(buf2, qarea, NT_G * g + t)));
+      ++n;
     }
   }
-  if constexpr (QR < 9) {
-    constexpr int W = qpitch_lds<NRG>() / 16;
-    constexpr int NL = (RB * W + 63) / 64;
-    nq += (NL - wave + 3) / 4;
-#pragma unroll 1
-    for (int j0 = 0; j0 < NL; j0 += 4) {
-      const int j = j0 + wave;
-      if (j < NL) {
-        const int c = 64 * j + lane;
-        const int row = c / W, part = c - W * (c / W);
-        // chunk part = 8p + 4h + lg of the row: dims 64(QR + p) + 16lg + 8h
-        const int dim = 64 * (QR + (part >> 3)) + 16 * (part & 3) + 8 * ((part >> 2) & 1);
-        const uint16_t* g = part < 8 * (9 - QR) ? src_of(row, dim) : q_base;
-        lds_dma16(reinterpret_cast<const uint8_t*>(g),
-                  __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(qlds + 1024 * j)));
+  return n;
+}
+
+// The staged query -> this wave's bf16 query fragments qf[g][s] (K-step s
+// of row group g).  An fp8 query is decoded exactly (E4M3 fits in bf16);
+// q_scale is folded into the score constant.
+template <int NRG, bool QF8>
+__device__ __forceinline__ void read_q(MLA_LDS uint8_t* buf2, MLA_LDS uint8_t* qarea, int lane,
+                                       bf16x8 (&qf)[NRG][18]) {
+#pragma unroll
+  for (int g = 0; g < NRG; ++g)
+#pragma unroll
+    for (int pp = 0; pp < 9; ++pp) {
+      if constexpr (QF8) {
+        const u32x4 raw = *(const MLA_LDS u32x4*)(q_block(buf2, qarea, 9 * g + pp) + 16 * lane);
+        qf[g][2 * pp] = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
+        qf[g][2 * pp + 1] = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
+      } else {
+        qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(q_block(buf2, qarea, 18 * g + 2 * pp) + 16 * lane);
+        qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(q_block(buf2, qarea, 18 * g + 2 * pp + 1) + 16 * lane);
       }
     }
-  }
-  return nq;
 }
 
 // A valid cache row among the first n staged indices (0 if there is none),
@@ -448,46 +395,23 @@ __device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_
 // S[g] (16 tokens x 16 rows, C layout: tokens 4*(l/16).. of row l%16) =
 // K . Q^T over the 576 dims, as 9 K-step pairs.  Step pp uses chunk 4pp+lg
 // of token 16*wave+lr (block (wave, pp) of the staged tile); K reads run
-// two steps ahead of their conversion, LDS-resident query fragments
-// MLA_QLDS_AHEAD steps ahead of their MFMAs, and each step interleaves its
-// MFMAs with the conversions of the next step.
-template <int NRG, int QR>
-__device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 (&qf)[NRG][2 * QR],
-                                        const MLA_LDS uint8_t* qlds, int wave, int lane, f32x4 (&S)[NRG]) {
+// two steps ahead of their conversion, and each step interleaves its MFMAs
+// with the conversions of the next step.
+template <int NRG>
+__device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 (&qf)[NRG][18], int wave, int lane,
+                                        f32x4 (&S)[NRG]) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
   const MLA_LDS uint8_t* kq = kt + tile_off(16 * wave + lr, lg);
-  const MLA_LDS uint8_t* qq = qlds + lr * qpitch_lds<NRG>() + 16 * lg - 128 * QR;
   u32x4 raw[3];
   raw[0] = *(const MLA_LDS u32x4*)kq;
   raw[1] = *(const MLA_LDS u32x4*)(kq + 1024);
-  // LDS-resident query fragments are read QLA K-steps ahead of their MFMAs
-  constexpr int QLA = MLA_QLDS_AHEAD;
-  bf16x8 ql[QLA + 1][NRG][2];
-#pragma unroll
-  for (int s0 = 0; s0 < QLA; ++s0) {
-    if (s0 >= QR && s0 < 9) {
-#pragma unroll
-      for (int g = 0; g < NRG; ++g)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ql[s0 % (QLA + 1)][g][h] = *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * s0 + 64 * h);
-    }
-  }
   bf16x8 klo = fp8x8_to_bf16x8(u32x2{raw[0][0], raw[0][1]});
   bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
 #pragma unroll
   for (int pp = 0; pp < 9; ++pp) {
     if (pp + 2 < 9) raw[(pp + 2) % 3] = *(const MLA_LDS u32x4*)(kq + 1024 * (pp + 2));
-    if (pp + QLA >= QR && pp + QLA < 9) {
-#pragma unroll
-      for (int g = 0; g < NRG; ++g)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ql[(pp + QLA) % (QLA + 1)][g][h] =
-              *(const MLA_LDS bf16x8*)(qq + 16 * g * qpitch_lds<NRG>() + 128 * (pp + QLA) + 64 * h);
-    }
     bf16x8 nlo = klo, nhi = khi;
     if (pp + 1 < 9) {
       nlo = fp8x8_to_bf16x8(u32x2{raw[(pp + 1) % 3][0], raw[(pp + 1) % 3][1]});
@@ -495,17 +419,12 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
     }
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
-      if (pp < QR) {
-        S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
-        S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
-      } else {
-        S[g] = mfma16(klo, ql[pp % (QLA + 1)][g][0], S[g]);
-        S[g] = mfma16(khi, ql[pp % (QLA + 1)][g][1], S[g]);
-      }
+      S[g] = mfma16(klo, qf[g][2 * pp], S[g]);
+      S[g] = mfma16(khi, qf[g][2 * pp + 1], S[g]);
     }
     klo = nlo;
     khi = nhi;
-    interleave<2 * NRG, 8, 3>();
+    interleave<2 * NRG, 8, 1>();
     __builtin_amdgcn_sched_barrier(0);  // keep the steps (and their read-ahead) in order
   }
 }
@@ -527,54 +446,16 @@ __device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const flo
   }
 }
 
-// fp8 query block staged at q8s (rows of Q8_PITCH bytes) -> the bf16 query
-// fragments of K-step pairs pp < QR (same dims as load order of the bf16
-// block) and, for the 48-row block, the LDS-resident dims [64 QR, 576) in
-// their read order at qlds.  E4M3 -> bf16 is exact; q_scale is folded into
-// the score constant.  The caller publishes qlds with a barrier.
-template <int NRG, int QR>
-__device__ __forceinline__ void decode_q8(const MLA_LDS uint8_t* q8s, MLA_LDS uint8_t* qlds, int tid, int lr,
-                                          int lg, bf16x8 (&qf)[NRG][2 * QR]) {
-  constexpr int RB = 16 * NRG;
-#pragma unroll
-  for (int g = 0; g < NRG; ++g) {
-    const MLA_LDS uint8_t* src = q8s + (16 * g + lr) * Q8_PITCH + 16 * lg;
-#pragma unroll
-    for (int pp = 0; pp < QR; ++pp) {
-      const u32x4 raw = *(const MLA_LDS u32x4*)(src + 64 * pp);
-      qf[g][2 * pp] = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
-      qf[g][2 * pp + 1] = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
-    }
-  }
-  if constexpr (QR < 9) {
-    // (row, pair, lane group): 16 dims -> chunks 8p + lg (first 8) and
-    // 8p + 4 + lg (next 8) of the row's LDS part
-    constexpr int NP = 9 - QR;
-#pragma unroll 1
-    for (int e = tid; e < RB * NP * 4; e += 256) {
-      const int row = e / (NP * 4), rem = e - (NP * 4) * row;
-      const int pq = rem >> 2, l4 = rem & 3;
-      const u32x4 raw = *(const MLA_LDS u32x4*)(q8s + row * Q8_PITCH + 64 * (QR + pq) + 16 * l4);
-      MLA_LDS uint8_t* dst = qlds + row * qpitch_lds<NRG>() + 16 * (8 * pq + l4);
-      *(MLA_LDS bf16x8*)dst = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
-      *(MLA_LDS bf16x8*)(dst + 64) = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
-    }
-  }
-}
-
 template <int NRG, bool QF8, bool PLAN>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl) {
   constexpr int RB = 16 * NRG;
-  constexpr int QR = qreg_pairs<NRG>();
-  constexpr int QS = qstage_pairs<NRG>();
-  constexpr int QL_BYTES = QS < 9 && !(QF8 && QR == 9) ? ((RB * (qpitch_lds<NRG>() / 16) + 63) / 64) * 1024 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t pt[2 * PT_ELEMS];  // double buffered by tile parity
   __shared__ __attribute__((aligned(16))) float redmax[RB * 4];
   __shared__ __attribute__((aligned(16))) float redsum[RB * 4];
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
-  __shared__ __attribute__((aligned(16))) uint8_t qlds_[QL_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t qarea_[q_area_bytes<NRG, QF8>()];  // query staging, past tile buffer 2
   __shared__ int32_t red_i[4];
   __shared__ int64_t rowoff[RB];  // output offset of block row i within its request, -1 past M
   // the normalised O rows are staged as bf16 [RB][O_PITCH] in the tile buffers
@@ -585,7 +466,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   const int lr = lane & 15, lg = lane >> 4;
   MLA_LDS uint8_t* kbuf = (MLA_LDS uint8_t*)kbuf_;
   MLA_LDS int32_t* idxl = (MLA_LDS int32_t*)idx;
-  MLA_LDS uint8_t* qlds = (MLA_LDS uint8_t*)qlds_;
+  MLA_LDS uint8_t* qarea = (MLA_LDS uint8_t*)qarea_;
   const VOffsets vo = v_offsets(wave, lane);
 
   // ---- block -> (worker, row block); the row blocks of a worker share an
@@ -744,15 +625,16 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       L = p.indptr[r + 1] - p.indptr[r];
     }
     const int64_t V = P + W * (r + 1);  // stream position of the request's first token
+    const int64_t vq = div_pos(V, chunk);  // the unit that holds it
     if (L == 0) {
-      const int64_t owner = V / chunk < nunits - 1 ? V / chunk : nunits - 1;
+      const int64_t owner = vq < nunits - 1 ? vq : nunits - 1;
       if (owner == u) fill_neginf(r, 0);
       continue;
     }
     const int a = (int)((g0 > V ? g0 : V) - V);
     const int b = (int)((g1 < V + L ? g1 : V + L) - V);
     if (b <= a) continue;
-    const int k = (a == 0) ? 0 : (int)((V + a) / chunk - V / chunk);
+    const int k = (a == 0) ? 0 : (int)(u - vq);  // a > 0: the piece starts at this unit's start
     if (PLAN && k >= p.num_splits) {
       // only a host copy of the offsets that differs from kv_indptr gets
       // here: poison the rows' last split instead of writing past it
@@ -765,7 +647,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       continue;
     }
     if (k == 0) {
-      const int nsplit = (int)((V + L - 1) / chunk - V / chunk + 1);
+      const int nsplit = (int)(div_pos(V + L - 1, chunk) - vq + 1);
       if (nsplit < p.num_splits) fill_neginf(r, nsplit);
     }
 
@@ -783,13 +665,16 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     }
     lim_min = wave_min64(lim_min);  // wave-uniform: keep the mask test scalar
 
-    // ---- stage the first segment's cache indices and the block's query
-    // rows in LDS with direct global->LDS loads; the register part of the
-    // query goes to tile buffer 2 (tile 2 is issued only after every wave
-    // has read it).  Only the indices are waited for here: tiles 0 and 1
-    // are issued while the query is still in flight.
-    MLA_LDS uint8_t* qst = kbuf + 2 * TILE_BYTES;
-    const int nq = stage_q_and_idx<NRG, QF8>(p, r, m_lo, rows_r + a, min(IDX_CAP, b - a), qst, qlds, idxl, wave, lane);
+    // ---- stage the first segment's cache indices and the block's query in
+    // LDS by direct loads (the query in tile buffer 2 and the query area;
+    // tile 2 is issued only after every wave has read it).  Only the indices
+    // are waited for here: tiles 0 and 1 are issued while the query is still
+    // in flight.
+    int64_t rowq[NRG];
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) rowq[g] = ((int64_t)r * p.qlen + rj[g]) * p.q_sr + (int64_t)rh[g] * p.q_sh;
+    const int nq = stage_q_and_idx<NRG, QF8>(p, rowq, rows_r + a, min(IDX_CAP, b - a), kbuf + 2 * TILE_BYTES, qarea,
+                                             idxl, wave, lane);
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
     rp_ready = true;  // the planned offsets were loaded before this staging
@@ -808,38 +693,15 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         wait_vm_all();
       __syncthreads();
     }
-    // query fragments for K-step pairs pp < QR: K-step 2pp uses dims
-    // 64pp+16lg..+7, 2pp+1 the next 8 (the K fragments use the same order)
-    bf16x8 qf[NRG][2 * QR];
-    if constexpr (QF8) {
-      decode_q8<NRG, QR>(qst, qlds, tid, lr, lg, qf);
-      if constexpr (QR < 9) __syncthreads();  // the decoded LDS part is complete
-    } else {
-#pragma unroll
-      for (int g = 0; g < NRG; ++g) {
-        const MLA_LDS uint8_t* src = qst + (16 * g + lr) * qpitch_reg<NRG>() + 32 * lg;
-#pragma unroll
-        for (int pp = 0; pp < (QR < QS ? QR : QS); ++pp) {
-          qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src + 128 * pp);
-          qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src + 128 * pp + 16);
-        }
-        // pairs staged in the query area (read order: chunk 4h + lg of a
-        // pair holds dims 16lg + 8h .. +7 of it)
-        const MLA_LDS uint8_t* src2 = qlds + (16 * g + lr) * qpitch_lds<NRG>() + 16 * lg;
-#pragma unroll
-        for (int pp = QS; pp < QR; ++pp) {
-          qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(src2 + 128 * (pp - QS));
-          qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(src2 + 128 * (pp - QS) + 64);
-        }
-      }
-    }
-    // keep the query fragments in AGPRs (they are only MFMA B operands), so
-    // the arch VGPRs hold the per-tile working set
+    // the query fragments: K-step 2pp uses dims 64pp+16lg..+7, 2pp+1 the
+    // next 8 (the K fragments use the same order); kept in AGPRs (they are
+    // only MFMA B operands), so the arch VGPRs hold the per-tile working set
+    bf16x8 qf[NRG][18];
+    read_q<NRG, QF8>(kbuf + 2 * TILE_BYTES, qarea, lane, qf);
 #pragma unroll
     for (int g = 0; g < NRG; ++g)
 #pragma unroll
-      for (int ss = 0; ss < 2 * (NRG >= 3 && QPIN3 < QR ? QPIN3 : QR); ++ss) asm volatile("" : "+a"(qf[g][ss]));
-
+      for (int ss = 0; ss < 18; ++ss) asm volatile("" : "+a"(qf[g][ss]));
 
     f32x4 O[8][NRG];
     // per row: the softmax reference (log2 units) and its negation, the
@@ -906,7 +768,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
         const int nrow = it + 2 < ntiles ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
         f32x4 S[NRG];
-        qk_tile<NRG, QR>(kt, qf, qlds, wave, lane, S);
+        qk_tile<NRG>(kt, qf, wave, lane, S);
         // ---- mask (raw score units) only where a row's visible range or a
         // bad index reaches into this quarter
         {
