@@ -16,6 +16,8 @@
  *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
  *   mla_decode_partial_hostplan, mla_decode_partial_fp8q_hostplan  the two
  *                       above with the split partition computed on the host
+ *   mla_decode_attend   the attention and the LSE merge in one launch ->
+ *                       latent (bf16) and LSE, with a caller's workspace
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
  *   mla_merge_value_gate  the merge, W_UV and gate in one call (no latent written)
@@ -266,6 +268,51 @@ int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_stride_row, in
                                      uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                                      float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
                                      const int32_t* kv_indptr_host, void* stream);
+
+/*
+ * The attention and its LSE merge in one launch ([MLA] `m1c_inputs`: the
+ * mono kernel runs the partials, then merges the splits): the merged latent
+ * and LSE of mla_decode_partial_hostplan followed by mla_merge_lse, bit for
+ * bit, without the partials as outputs.
+ *   o    [S][...][512] bf16, strides (o_row, o_head): row t, head h gets
+ *        bf16(sum_k e^(LSE_k - LSE) o_k) over the splits k of its request
+ *        (0 where every split is empty, the canonical NaN 0x7FC0 where a
+ *        split is NaN)
+ *   lse  [S][...] f32, strides (l_row, l_head), or NULL: the merged LSE
+ *        (natural log; -inf for a row that sees no token)
+ *   workspace  device memory of at least mla_decode_attend_workspace_bytes
+ *        bytes, 256-byte aligned: a counter per (request, 48-row block),
+ *        then the partials of the requests that take more than one split.
+ *        Its first part (the counters, 4*batch*row_blocks bytes rounded up
+ *        to 256) must be zero before the first call on it; every call that
+ *        completes with a consistent kv_indptr_host leaves it zero again.
+ *        Calls that overlap on one workspace race.
+ * The other arguments, the split partition and the query layout are those
+ * of mla_decode_partial_hostplan (bf16 query).  A request whose tokens fall
+ * in one split is written straight to o; for a split request, the last of
+ * its pieces to finish (counted with a system-scope atomic, the partial rows
+ * written and read with system-coherent accesses) merges its splits in the
+ * LSE merge's order.
+ * Errors: those of mla_decode_partial_hostplan; MLA_ERR_INVALID for a null
+ * o, workspace or kv_indptr_host (batch > 0) or workspace_bytes below the
+ * size it needs; MLA_ERR_UNSUPPORTED for more than 256 workers, a unit of
+ * more than 65535 requests, o not 16-byte aligned with strides that are
+ * multiples of 8, a workspace not 256-byte aligned, or a workspace of 2 GiB
+ * or more.
+ */
+int mla_decode_attend(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head, int32_t batch,
+                      int32_t qlen, int32_t heads, const uint8_t* kv_cache, int64_t num_slots,
+                      const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float kv_scale,
+                      int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                      const int32_t* kv_indptr_host, uint16_t* o, int64_t o_row, int64_t o_head, float* lse,
+                      int64_t l_row, int64_t l_head, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * The workspace mla_decode_attend needs for these sizes (bytes), or
+ * -MLA_ERR_INVALID for batch < 0, qlen < 1, heads < 1 or num_workers < 1.
+ * Host only; it depends on the sizes alone (not on the request lengths).
+ */
+int64_t mla_decode_attend_workspace_bytes(int32_t batch, int32_t qlen, int32_t heads, int32_t num_workers);
 
 /*
  * Host helper: the split partition mla_decode_partial uses.

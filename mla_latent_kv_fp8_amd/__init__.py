@@ -58,12 +58,17 @@ def lib() -> ctypes.CDLL:
         L.mla_merge_value_gate.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, P, i64, i64, P, i64,
                                            i64, P, i64, P, i32, i32, i32, P, i64, P, i64, i64, P]
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.mla_decode_attend.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32, i32, P, P, i64,
+                                        i64, P, i64, i64, P, i64, P]
+        L.mla_decode_attend_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.mla_decode_attend_workspace_bytes.restype = ctypes.c_int64
         L.mla_merge_lse.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, i32, P, i64, i64, P,
                                     i64, i64, P]
         L.mla_value_gate.argtypes = [P, i64, i64, i32, P, i64, i64, P, i64, i64, P, i64, P, i32, i32, i32,
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
-                     "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate"):
+                     "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate",
+                     "mla_decode_attend"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -203,6 +208,57 @@ def decode_partial_hostplan(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: 
     decode_partial with the split partition computed on the host from
     kv_indptr_host."""
     decode_partial(q, kv_cache, kv_indptr, kv_indices, o_part, lse_part, kv_indptr_host=kv_indptr_host, **kw)
+
+
+def decode_attend_workspace_bytes(batch: int, qlen: int, heads: int, num_workers: int) -> int:
+    """mla_decode_attend_workspace_bytes: the workspace decode_attend needs."""
+    n = lib().mla_decode_attend_workspace_bytes(int(batch), int(qlen), int(heads), int(num_workers))
+    if n < 0:
+        _check(-n, "mla_decode_attend_workspace_bytes")
+    return int(n)
+
+
+def _attend_args(q, kv_cache, kv_indptr, kv_indices, o, lse, *, qlen, heads, sm_scale, kv_scale, num_splits,
+                 num_workers, split_min_tokens, kv_indptr_host):
+    S = q.shape[0]
+    batch = kv_indptr.shape[0] - 1
+    if S != batch * qlen:
+        raise MlaError("q has %d rows, expected batch*qlen = %d" % (S, batch * qlen))
+    if q.shape[-1] != D_QK or q.shape[1] < heads:
+        raise MlaError("q must be [S, >=heads, 576]")
+    if o.shape[0] < S or o.shape[1] < heads or o.shape[2] != D_LATENT:
+        raise MlaError("o must be [S, >=heads, 512]")
+    if lse is not None and (lse.shape[0] < S or lse.shape[1] < heads):
+        raise MlaError("lse must be [S, >=heads]")
+    ih = np.ascontiguousarray(kv_indptr_host, dtype=np.int32)
+    if ih.shape != (batch + 1,):
+        raise MlaError("kv_indptr_host must hold batch+1 offsets")
+    head = (_dev(q, "q", _BF16), q.stride(0), q.stride(1), batch, qlen, heads, _dev(kv_cache, "kv_cache", _U8),
+            kv_cache.shape[0], _dev(kv_indptr, "kv_indptr", (torch.int32,)),
+            _dev(kv_indices, "kv_indices", (torch.int32,)), float(sm_scale), float(kv_scale), int(num_splits),
+            int(num_workers), int(split_min_tokens), ih.ctypes.data_as(ctypes.c_void_p),
+            _dev(o, "o", _BF16), o.stride(0), o.stride(1))
+    tail = ((_dev(lse, "lse", (torch.float32,)), lse.stride(0), lse.stride(1)) if lse is not None
+            else (None, 0, 0))
+    return head + tail, ih
+
+
+def decode_attend(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                  o: torch.Tensor, lse: torch.Tensor | None, workspace: torch.Tensor, kv_indptr_host: np.ndarray, *,
+                  qlen: int, heads: int, sm_scale: float, kv_scale: float, num_splits: int,
+                  num_workers: int = 256, split_min_tokens: int = 256) -> None:
+    """mla_decode_attend: the partials and their LSE merge in one launch ->
+    o [S, heads, 512] bf16 (the merged latent) and lse [S, heads] f32 (or
+    None), bit for bit decode_partial (host plan) + merge_lse.  workspace: a
+    uint8 device tensor of at least decode_attend_workspace_bytes bytes whose
+    counter part is zero before its first use (torch.zeros)."""
+    args, ih = _attend_args(q, kv_cache, kv_indptr, kv_indices, o, lse, qlen=qlen, heads=heads, sm_scale=sm_scale,
+                            kv_scale=kv_scale, num_splits=num_splits, num_workers=num_workers,
+                            split_min_tokens=split_min_tokens, kv_indptr_host=kv_indptr_host)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise MlaError("workspace must be a contiguous uint8 tensor")
+    st = lib().mla_decode_attend(*args, _dev(workspace, "workspace", _U8), workspace.numel(), _stream())
+    _check(st, "mla_decode_attend")
 
 
 def split_plan(kv_indptr, num_splits: int, num_workers: int, split_min_tokens: int):

@@ -37,7 +37,11 @@
 //    contraction uses the matching token permutation).
 //  * Epilogue: O is normalised into LDS as bf16 rows and written out one
 //    whole 1 KB row per store instruction.
-#include "common.hpp"
+//  * The fused call (mla_decode_attend) also merges: a request of one split
+//    goes straight to the merged latent; the pieces of a split request go to
+//    workspace slots, and the block that completes a request's count (a
+//    system-scope atomic) merges its splits with the LSE merge's own code.
+#include "post_common.hpp"
 
 namespace mla {
 
@@ -61,6 +65,16 @@ struct PartialArgs {
   int64_t os_s, os_r, os_h;
   float* lse;
   int64_t ls_s, ls_r, ls_h;
+  // the fused call: the merged latent and LSE (lat_lse may be null), and the
+  // workspace (counters, then the split partials by unit slot)
+  uint16_t* lat;
+  int64_t lat_r, lat_h;
+  float* lat_lse;
+  int64_t ll_r, ll_h;
+  int32_t* ws_cnt;      // one counter per (request, row block)
+  uint8_t* ws;          // base of the partial area
+  int32_t ws_lse_off;   // byte offset of the partial LSEs [slot][RB] in ws
+  int32_t ws_o_off;     // byte offset of the partial rows [slot][RB][512] bf16 in ws
 };
 
 // The split partition computed on the host (the one the kernel derives from
@@ -446,8 +460,9 @@ __device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const flo
   }
 }
 
-template <int NRG, bool QF8, bool PLAN>
+template <int NRG, bool QF8, bool PLAN, bool FUSE>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl) {
+  static_assert(!FUSE || PLAN, "the fused call takes the host-built partition");
   constexpr int RB = 16 * NRG;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
   constexpr int PT_ELEMS = 2 * NRG * 64 * 8;  // P^T of one tile (bf16)
@@ -458,6 +473,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   __shared__ __attribute__((aligned(16))) uint8_t qarea_[q_area_bytes<NRG, QF8>()];  // query staging, past tile buffer 2
   __shared__ int32_t red_i[4];
   __shared__ int64_t rowoff[RB];  // output offset of block row i within its request, -1 past M
+  __shared__ int64_t latoff[FUSE ? RB : 1];  // the same in the merged latent
+  __shared__ int32_t last_[1];               // fused call: the counter value this block saw
   // the normalised O rows are staged as bf16 [RB][O_PITCH] in the tile buffers
   constexpr int O_PITCH = MLA_D_LATENT + 16;  // +32 B: rows start 8 banks apart
   static_assert(RB * O_PITCH * 2 <= NBUF * TILE_BYTES, "O staging fits the tile buffers");
@@ -569,7 +586,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   const int64_t g1 = g0 + chunk < Tv ? g0 + chunk : Tv;
   if (tid < RB) {
     const int m = m_lo + tid;
-    rowoff[tid] = m < p.M ? (int64_t)(m / p.heads) * p.os_r + (int64_t)(m % p.heads) * p.os_h : -1;
+    rowoff[tid] = FUSE ? 0 : (m < p.M ? (int64_t)(m / p.heads) * p.os_r + (int64_t)(m % p.heads) * p.os_h : -1);
+    if constexpr (FUSE) latoff[tid] = m < p.M ? (int64_t)(m / p.heads) * p.lat_r + (int64_t)(m % p.heads) * p.lat_h : -1;
   }
   __syncthreads();
   if (u >= nunits) return;
@@ -628,14 +646,34 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     const int64_t vq = div_pos(V, chunk);  // the unit that holds it
     if (L == 0) {
       const int64_t owner = vq < nunits - 1 ? vq : nunits - 1;
-      if (owner == u) fill_neginf(r, 0);
+      if (owner == u) {
+        if constexpr (FUSE) {
+          // an empty request's merged rows: latent 0, LSE -inf
+          const int nrows = min(RB, p.M - m_lo);
+          uint16_t* lbase = p.lat + (int64_t)r * p.qlen * p.lat_r + 8 * lane;
+          for (int i = wave; i < nrows; i += 4) *reinterpret_cast<u32x4*>(lbase + latoff[i]) = u32x4{0, 0, 0, 0};
+          if (p.lat_lse && tid < nrows) {
+            const int m = m_lo + tid;
+            p.lat_lse[((int64_t)r * p.qlen + m / p.heads) * p.ll_r + (int64_t)(m % p.heads) * p.ll_h] = -INFINITY;
+          }
+        } else {
+          fill_neginf(r, 0);
+        }
+      }
       continue;
     }
     const int a = (int)((g0 > V ? g0 : V) - V);
     const int b = (int)((g1 < V + L ? g1 : V + L) - V);
     if (b <= a) continue;
     const int k = (a == 0) ? 0 : (int)(u - vq);  // a > 0: the piece starts at this unit's start
-    if (PLAN && k >= p.num_splits) {
+    // fused call: the request's split count, and this piece's workspace
+    // slot (split 0 is the last piece of unit vq: slot 1 of it; a later split
+    // is the first piece of its unit: slot 0)
+    const int nsplit = (int)(div_pos(V + L - 1, chunk) - vq + 1);
+    const int64_t su = k == 0 ? vq : (int64_t)u;
+    const int slot = (int)((su * 2 + (k == 0 ? 1 : 0)) * p.n_rb + rb);
+    if (FUSE && (k >= p.num_splits || su < 0 || su >= nunits)) continue;  // a host copy that differs from kv_indptr
+    if (!FUSE && PLAN && k >= p.num_splits) {
       // only a host copy of the offsets that differs from kv_indptr gets
       // here: poison the rows' last split instead of writing past it
       const int nrows = min(RB, p.M - m_lo);
@@ -646,10 +684,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       }
       continue;
     }
-    if (k == 0) {
-      const int nsplit = (int)(div_pos(V + L - 1, chunk) - vq + 1);
-      if (nsplit < p.num_splits) fill_neginf(r, nsplit);
-    }
+    if (!FUSE && k == 0 && nsplit < p.num_splits) fill_neginf(r, nsplit);
 
     // ---------------------------------------------------------- one piece
     const int32_t* rows_r = p.indices + (PLAN ? base + (int)P : p.indptr[r]);
@@ -840,8 +875,14 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // The row sums; O normalised to bf16 into LDS (every wave is past its
     // last PV after the first barrier, so the tile buffers are free), then
     // written out one whole 1 KB row per store instruction.
+    // The fused call writes a request of one split straight into the merged
+    // latent (what the merge makes of one split: rows with no visible token
+    // are 0, NaN rows the canonical NaN) and the pieces of a split request
+    // into its workspace slot; the last of them to finish merges them.
+    const bool direct = FUSE && nsplit == 1;
     MLA_LDS uint16_t* ost = (MLA_LDS uint16_t*)kbuf;
-    uint64_t wmask = 0;  // block rows to write (a finite or NaN sum, row < M)
+    uint64_t wmask = 0;  // block rows to write (a finite or NaN sum, row < M; every row < M when direct)
+    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(p.ws, 0, 0x7FFFFFFF, 0x00020000);
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
       const f32x4 s4 = *reinterpret_cast<const f32x4*>(&redsum[(16 * g + lr) * 4]);
@@ -849,49 +890,122 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       // l == 0: no visible token in this split (the row is not written).  A
       // NaN l (NaN cache bytes or an invalid index) is written through, so
       // it poisons the row.
-      const float inv = p.kv_scale * __builtin_amdgcn_rcpf(l);
+      const float inv = direct && l == 0.0f ? 0.0f : p.kv_scale * __builtin_amdgcn_rcpf(l);
+      const bool nan_row = direct && l != l;
       MLA_LDS uint16_t* orow = ost + (16 * g + lr) * O_PITCH + 128 * wave + 4 * lg;
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const f32x4 v = O[d][g];
-        *reinterpret_cast<MLA_LDS u32x2*>(orow + 16 * d) =
-            u32x2{pk_bf16(v[0] * inv, v[1] * inv), pk_bf16(v[2] * inv, v[3] * inv)};
+        u32x2 w2 = u32x2{pk_bf16(v[0] * inv, v[1] * inv), pk_bf16(v[2] * inv, v[3] * inv)};
+        if (nan_row) w2 = u32x2{0x7FC07FC0u, 0x7FC07FC0u};
+        *reinterpret_cast<MLA_LDS u32x2*>(orow + 16 * d) = w2;
       }
       const int m = m_lo + 16 * g + lr;
-      wmask |= (__ballot(l != 0.0f && m < p.M) & 0xFFFFull) << (16 * g);  // lanes lg == 0: rows 16g + lr
+      wmask |= (__ballot((direct || l != 0.0f) && m < p.M) & 0xFFFFull) << (16 * g);  // lanes lg == 0: rows 16g + lr
       if (wave == 0 && lg == 0 && m < p.M) {
         const int t = r * p.qlen + rj[g], h = rh[g];
-        p.lse[k * p.ls_s + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h] =
-            l != 0.0f ? (mref[g] + __log2f(l)) * kLn2 : -INFINITY;
+        const float lv = l != 0.0f ? (mref[g] + __log2f(l)) * kLn2 : -INFINITY;
+        if constexpr (!FUSE) {
+          p.lse[k * p.ls_s + (int64_t)t * p.ls_r + (int64_t)h * p.ls_h] = lv;
+        } else if (direct) {
+          if (p.lat_lse) p.lat_lse[(int64_t)t * p.ll_r + (int64_t)h * p.ll_h] = lv;
+        } else {
+          // system-coherent store: the merging block may run on another XCD
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lv), wsr,
+                                                p.ws_lse_off + (slot * RB + 16 * g + lr) * 4, 0, 17);
+        }
       }
     }
     __syncthreads();
     {
       // this wave's rows wave, wave+4, ...: all LDS reads first, then the stores
-      uint16_t* obase = p.o + k * p.os_s + (int64_t)r * p.qlen * p.os_r + 8 * lane;
+      uint16_t* obase = FUSE ? p.lat + (int64_t)r * p.qlen * p.lat_r + 8 * lane
+                             : p.o + k * p.os_s + (int64_t)r * p.qlen * p.os_r + 8 * lane;
       const int wu = __builtin_amdgcn_readfirstlane(wave);
       u32x4 ov[RB / 4];
       int64_t off[RB / 4];
 #pragma unroll
       for (int j = 0; j < RB / 4; ++j) {
         ov[j] = *reinterpret_cast<const MLA_LDS u32x4*>(ost + (wu + 4 * j) * O_PITCH + 8 * lane);
-        off[j] = rowoff[wu + 4 * j];
+        off[j] = FUSE ? latoff[wu + 4 * j] : rowoff[wu + 4 * j];
       }
       // keep the reads together, ahead of the (conditional) stores
 #pragma unroll
       for (int j = 0; j < RB / 4; ++j) asm volatile("" : "+v"(ov[j]), "+v"(off[j]));
+      if (!FUSE || direct) {
 #pragma unroll
-      for (int j = 0; j < RB / 4; ++j)
-        if ((wmask >> (wu + 4 * j)) & 1) *reinterpret_cast<u32x4*>(obase + off[j]) = ov[j];
+        for (int j = 0; j < RB / 4; ++j)
+          if ((wmask >> (wu + 4 * j)) & 1) *reinterpret_cast<u32x4*>(obase + off[j]) = ov[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < RB / 4; ++j)
+          if ((wmask >> (wu + 4 * j)) & 1)
+            __builtin_amdgcn_raw_buffer_store_b128(ov[j], wsr, p.ws_o_off + (slot * RB + wu + 4 * j) * 1024 + 16 * lane,
+                                                   0, 17);
+      }
+    }
+    if constexpr (FUSE) {
+      if (!direct) {
+        // Count this piece in once its rows are complete in memory (every
+        // wave waits for its own system-coherent stores before the barrier);
+        // the block that completes the count merges the request's splits,
+        // reading them with system-coherent loads, and clears the counter
+        // for the next call.
+        wait_vm_all();
+        __syncthreads();
+        int32_t* cnt = p.ws_cnt + (int64_t)r * p.n_rb + rb;
+        if (tid == 0) last_[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __syncthreads();
+        if (last_[0] == nsplit - 1) {
+          const int nrows = min(RB, p.M - m_lo);
+          auto slot_of = [&](int kk) -> int {
+            return (int)((((kk == 0 ? vq : vq + kk) * 2) + (kk == 0 ? 1 : 0)) * p.n_rb + rb);
+          };
+#pragma unroll 1
+          for (int gi = 0; gi < RB / 16; ++gi) {
+            int rw[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = wave + 4 * (4 * gi + j);
+              rw[j] = row < nrows ? row : 0;
+            }
+            auto lse_at = [&](int j, int kk) -> float {
+              return __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(wsr, p.ws_lse_off + (slot_of(kk) * RB + rw[j]) * 4, 0, 17));
+            };
+            auto o_at = [&](int j, int kk) -> u32x4 {
+              return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   wsr, p.ws_o_off + (slot_of(kk) * RB + rw[j]) * 1024 + 16 * lane, 0, 17));
+            };
+            float l1[4];
+            merge_lse_load_at<4>(lse_at, nsplit, lane, l1);
+            u32x4 out[4];
+            float total[4];
+            merge_rows_at<4, false>(lse_at, o_at, nsplit, lane, l1, out, total);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int row = wave + 4 * (4 * gi + j);
+              if (row < nrows) {
+                *reinterpret_cast<u32x4*>(p.lat + (int64_t)r * p.qlen * p.lat_r + latoff[row] + 8 * lane) = out[j];
+                if (p.lat_lse && lane == 0) {
+                  const int m = m_lo + row;
+                  p.lat_lse[((int64_t)r * p.qlen + m / p.heads) * p.ll_r + (int64_t)(m % p.heads) * p.ll_h] = total[j];
+                }
+              }
+            }
+          }
+          if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+      }
     }
     __syncthreads();
   }
 }
 
-template <int NRG, bool QF8, bool PLAN>
+template <int NRG, bool QF8, bool PLAN, bool FUSE = false>
 static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, int blocks, hipStream_t s) {
   static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
-  hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN>), dim3(blocks), dim3(256), 0, s, a, pl);
+  hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, a, pl);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -972,8 +1086,43 @@ extern "C" int mla_split_plan(const int32_t* indptr, int32_t batch, int32_t num_
 
 namespace mla {
 
-// Argument checks, launch geometry and launch shared by the bf16- and
-// fp8-query entry points.  q_scale multiplies every score (1 for bf16).
+// Argument checks and kernel arguments shared by the partial and the fused
+// entry points (bf16 or fp8 query).  q_scale multiplies every score (1 for
+// bf16).  Sets the row-block geometry.
+static int common_args(PartialArgs& a, int& nrg, int& blocks, const void* q, bool q_fp8, int64_t q_stride_row,
+                       int64_t q_stride_head, float q_scale, int32_t batch, int32_t qlen, int32_t heads,
+                       const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, float sm_scale, float kv_scale, int32_t num_splits,
+                       int32_t num_workers, int32_t split_min_tokens) {
+  if (!q || !kv_cache || !kv_indptr || !kv_indices) return MLA_ERR_INVALID;
+  if (num_slots < 1 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
+  if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f) || kv_scale == INFINITY || sm_scale == INFINITY)
+    return MLA_ERR_INVALID;
+  if (!(q_scale > 0.0f) || q_scale == INFINITY) return MLA_ERR_INVALID;
+  // 16-byte query chunks (8 bf16 or 16 fp8 elements), 16-byte cache rows
+  const int64_t q_align = q_fp8 ? 16 : 8;
+  if ((q_stride_row | q_stride_head) % q_align != 0 || ((uintptr_t)q) % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (((uintptr_t)kv_cache) % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  const int64_t M = (int64_t)qlen * heads;
+  if (M > (1 << 20)) return MLA_ERR_UNSUPPORTED;
+  // rows per block: 16, 32 or 48 (larger requests take several blocks)
+  nrg = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
+  const int n_rb = (int)((M + 16 * nrg - 1) / (16 * nrg));
+  const int64_t nb = (int64_t)num_workers * n_rb;
+  if (nb > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
+  blocks = (int)nb;
+  a = PartialArgs{};
+  a.q = q_fp8 ? nullptr : (const uint16_t*)q;
+  a.q8 = q_fp8 ? (const uint8_t*)q : nullptr;
+  a.q_sr = q_stride_row; a.q_sh = q_stride_head;
+  a.batch = batch; a.qlen = qlen; a.heads = heads; a.M = (int32_t)M; a.n_rb = n_rb;
+  a.kv = kv_cache; a.num_slots = num_slots; a.indptr = kv_indptr; a.indices = kv_indices;
+  a.c_log2 = sm_scale * kv_scale * q_scale * kLog2e;  // q_scale = 1: sm_scale * kv_scale * log2(e)
+  a.kv_scale = kv_scale;
+  a.num_splits = num_splits; a.num_workers = num_workers; a.split_min = split_min_tokens;
+  return MLA_OK;
+}
+
 static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, int64_t q_stride_head,
                                float q_scale, int32_t batch, int32_t qlen, int32_t heads,
                                const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
@@ -985,34 +1134,14 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (batch < 0 || qlen < 1 || heads < 1 || num_splits < 1 || num_splits > 1024 || num_workers < 1)
     return MLA_ERR_INVALID;
   if (batch == 0) return MLA_OK;
-  if (!q || !kv_cache || !kv_indptr || !kv_indices || !o_part || !lse_part) return MLA_ERR_INVALID;
-  if (num_slots < 1 || num_slots > 0x7FFFFFFFLL) return MLA_ERR_INVALID;
-  if (!(kv_scale > 0.0f) || !(sm_scale > 0.0f) || kv_scale == INFINITY || sm_scale == INFINITY)
-    return MLA_ERR_INVALID;
-  if (!(q_scale > 0.0f) || q_scale == INFINITY) return MLA_ERR_INVALID;
-  // 16-byte query chunks (8 bf16 or 16 fp8 elements), 8-byte partial
-  // stores, 16-byte cache rows
-  const int64_t q_align = q_fp8 ? 16 : 8;
-  if ((q_stride_row | q_stride_head) % q_align != 0 || ((uintptr_t)q) % 16 != 0) return MLA_ERR_UNSUPPORTED;
-  if ((os_split | os_row | os_head) % 4 != 0 || ((uintptr_t)o_part) % 8 != 0) return MLA_ERR_UNSUPPORTED;
-  if (((uintptr_t)kv_cache) % 16 != 0) return MLA_ERR_UNSUPPORTED;
-  const int64_t M = (int64_t)qlen * heads;
-  if (M > (1 << 20)) return MLA_ERR_UNSUPPORTED;
-  // rows per block: 16, 32 or 48 (larger requests take several blocks)
-  const int nrg = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
-  const int n_rb = (int)((M + 16 * nrg - 1) / (16 * nrg));
-  const int64_t blocks = (int64_t)num_workers * n_rb;
-  if (blocks > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
-
+  if (!o_part || !lse_part) return MLA_ERR_INVALID;
   PartialArgs a;
-  a.q = q_fp8 ? nullptr : (const uint16_t*)q;
-  a.q8 = q_fp8 ? (const uint8_t*)q : nullptr;
-  a.q_sr = q_stride_row; a.q_sh = q_stride_head;
-  a.batch = batch; a.qlen = qlen; a.heads = heads; a.M = (int32_t)M; a.n_rb = n_rb;
-  a.kv = kv_cache; a.num_slots = num_slots; a.indptr = kv_indptr; a.indices = kv_indices;
-  a.c_log2 = sm_scale * kv_scale * q_scale * kLog2e;  // q_scale = 1: sm_scale * kv_scale * log2(e)
-  a.kv_scale = kv_scale;
-  a.num_splits = num_splits; a.num_workers = num_workers; a.split_min = split_min_tokens;
+  int nrg = 3, blocks = 0;
+  int st = common_args(a, nrg, blocks, q, q_fp8, q_stride_row, q_stride_head, q_scale, batch, qlen, heads, kv_cache,
+                       num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens);
+  if (st != MLA_OK) return st;
+  // 8-byte partial stores
+  if ((os_split | os_row | os_head) % 4 != 0 || ((uintptr_t)o_part) % 8 != 0) return MLA_ERR_UNSUPPORTED;
   a.o = o_part; a.os_s = os_split; a.os_r = os_row; a.os_h = os_head;
   a.lse = lse_part; a.ls_s = ls_split; a.ls_r = ls_row; a.ls_h = ls_head;
   hipStream_t s = (hipStream_t)stream;
@@ -1020,36 +1149,98 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (indptr_host)
     for (int32_t r = 0; r < batch; ++r)
       if (indptr_host[r + 1] < indptr_host[r]) return MLA_ERR_INVALID;
-  const int st = indptr_host && num_workers <= PLAN_UNITS
-                     ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
-                     : MLA_ERR_UNSUPPORTED;
+  st = indptr_host && num_workers <= PLAN_UNITS
+           ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
+           : MLA_ERR_UNSUPPORTED;
   if (st == MLA_ERR_INVALID) return st;
   if (st == MLA_OK) {
     if (q_fp8) {
       switch (nrg) {
-        case 1: return launch<1, true, true>(a, pl, (int)blocks, s);
-        case 2: return launch<2, true, true>(a, pl, (int)blocks, s);
-        default: return launch<3, true, true>(a, pl, (int)blocks, s);
+        case 1: return launch<1, true, true>(a, pl, blocks, s);
+        case 2: return launch<2, true, true>(a, pl, blocks, s);
+        default: return launch<3, true, true>(a, pl, blocks, s);
       }
     }
     switch (nrg) {
-      case 1: return launch<1, false, true>(a, pl, (int)blocks, s);
-      case 2: return launch<2, false, true>(a, pl, (int)blocks, s);
-      default: return launch<3, false, true>(a, pl, (int)blocks, s);
+      case 1: return launch<1, false, true>(a, pl, blocks, s);
+      case 2: return launch<2, false, true>(a, pl, blocks, s);
+      default: return launch<3, false, true>(a, pl, blocks, s);
     }
   }
   const UnitPlan<false> none;
   if (q_fp8) {
     switch (nrg) {
-      case 1: return launch<1, true, false>(a, none, (int)blocks, s);
-      case 2: return launch<2, true, false>(a, none, (int)blocks, s);
-      default: return launch<3, true, false>(a, none, (int)blocks, s);
+      case 1: return launch<1, true, false>(a, none, blocks, s);
+      case 2: return launch<2, true, false>(a, none, blocks, s);
+      default: return launch<3, true, false>(a, none, blocks, s);
     }
   }
   switch (nrg) {
-    case 1: return launch<1, false, false>(a, none, (int)blocks, s);
-    case 2: return launch<2, false, false>(a, none, (int)blocks, s);
-    default: return launch<3, false, false>(a, none, (int)blocks, s);
+    case 1: return launch<1, false, false>(a, none, blocks, s);
+    case 2: return launch<2, false, false>(a, none, blocks, s);
+    default: return launch<3, false, false>(a, none, blocks, s);
+  }
+}
+
+// The fused call's workspace: the counters (one int32 per request and row
+// block), then the partial LSEs [slot][RB] f32 and rows [slot][RB][512] bf16
+// of two slots per unit and row block, each part 256-byte aligned.
+struct AttendLayout {
+  int64_t cnt_bytes, lse_bytes, o_bytes, total;
+};
+static AttendLayout attend_layout(int32_t batch, int32_t qlen, int32_t heads, int32_t num_workers) {
+  const int64_t M = (int64_t)qlen * heads;
+  const int nrg = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
+  const int64_t rb_rows = 16 * nrg, n_rb = (M + rb_rows - 1) / rb_rows;
+  const int64_t slots = 2 * (int64_t)(num_workers < PLAN_UNITS ? num_workers : PLAN_UNITS) * n_rb;
+  auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+  AttendLayout l;
+  l.cnt_bytes = al(4 * (int64_t)batch * n_rb);
+  l.lse_bytes = al(4 * slots * rb_rows);
+  l.o_bytes = slots * rb_rows * 1024;
+  l.total = l.cnt_bytes + l.lse_bytes + l.o_bytes;
+  return l;
+}
+
+static int attend_impl(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head, int32_t batch, int32_t qlen,
+                       int32_t heads, const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                       const int32_t* kv_indices, float sm_scale, float kv_scale, int32_t num_splits,
+                       int32_t num_workers, int32_t split_min_tokens, const int32_t* indptr_host, uint16_t* o,
+                       int64_t o_row, int64_t o_head, float* lse, int64_t l_row, int64_t l_head, void* workspace,
+                       int64_t workspace_bytes, void* stream) {
+  if (batch < 0 || qlen < 1 || heads < 1 || num_splits < 1 || num_splits > 1024 || num_workers < 1)
+    return MLA_ERR_INVALID;
+  if (batch == 0) return MLA_OK;
+  if (!o || !workspace || !indptr_host) return MLA_ERR_INVALID;
+  PartialArgs a;
+  int nrg = 3, blocks = 0;
+  int st = common_args(a, nrg, blocks, q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
+                       num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens);
+  if (st != MLA_OK) return st;
+  if (num_workers > PLAN_UNITS) return MLA_ERR_UNSUPPORTED;
+  // 16-byte latent row stores; a 256-byte aligned workspace addressed with
+  // 32-bit offsets
+  if ((o_row | o_head) % 8 != 0 || ((uintptr_t)o) % 16 != 0) return MLA_ERR_UNSUPPORTED;
+  if (((uintptr_t)workspace) % 256 != 0) return MLA_ERR_UNSUPPORTED;
+  const AttendLayout lay = attend_layout(batch, qlen, heads, num_workers);
+  if (lay.total > 0x7FFFFFFFLL) return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < lay.total) return MLA_ERR_INVALID;
+  for (int32_t r = 0; r < batch; ++r)
+    if (indptr_host[r + 1] < indptr_host[r]) return MLA_ERR_INVALID;
+  UnitPlan<true> pl;
+  st = make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl);
+  if (st != MLA_OK) return st;
+  a.lat = o; a.lat_r = o_row; a.lat_h = o_head;
+  a.lat_lse = lse; a.ll_r = l_row; a.ll_h = l_head;
+  a.ws_cnt = reinterpret_cast<int32_t*>(workspace);
+  a.ws = reinterpret_cast<uint8_t*>(workspace);
+  a.ws_lse_off = (int32_t)lay.cnt_bytes;
+  a.ws_o_off = (int32_t)(lay.cnt_bytes + lay.lse_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  switch (nrg) {
+    case 1: return launch<1, false, true, true>(a, pl, blocks, s);
+    case 2: return launch<2, false, true, true>(a, pl, blocks, s);
+    default: return launch<3, false, true, true>(a, pl, blocks, s);
   }
 }
 
@@ -1112,3 +1303,21 @@ extern "C" int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_str
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
                                   ls_split, ls_row, ls_head, stream, kv_indptr_host);
 }
+
+extern "C" int64_t mla_decode_attend_workspace_bytes(int32_t batch, int32_t qlen, int32_t heads, int32_t num_workers) {
+  if (batch < 0 || qlen < 1 || heads < 1 || num_workers < 1) return -MLA_ERR_INVALID;
+  return mla::attend_layout(batch, qlen, heads, num_workers).total;
+}
+
+extern "C" int mla_decode_attend(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head, int32_t batch,
+                                 int32_t qlen, int32_t heads, const uint8_t* kv_cache, int64_t num_slots,
+                                 const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float kv_scale,
+                                 int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                                 const int32_t* kv_indptr_host, uint16_t* o, int64_t o_row, int64_t o_head,
+                                 float* lse, int64_t l_row, int64_t l_head, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+  return mla::attend_impl(q, q_stride_row, q_stride_head, batch, qlen, heads, kv_cache, num_slots, kv_indptr,
+                          kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens, kv_indptr_host,
+                          o, o_row, o_head, lse, l_row, l_head, workspace, workspace_bytes, stream);
+}
+

@@ -48,17 +48,18 @@ __device__ __forceinline__ float wave_reduce(float x, F op) {
 // the LSEs in every pass.  ONE = true asserts at most 64 splits: that
 // variant has no loads before the latent rows', so a caller's loads issued
 // after merge_lse_load are not waited for until then.
-template <int R>
-__device__ __forceinline__ void merge_lse_load(const float* const* lp, int64_t ls_split, int num_splits, int lane,
-                                               float (&l1)[R]) {
+// The *_at forms take the split loads as functors: lse_at(r, k) loads row
+// r's split-k LSE, o_at(r, k) this lane's 8 columns (16 bytes) of its split-k
+// latent row; the strided forms below read the usual [split][row] layout.
+template <int R, class LA>
+__device__ __forceinline__ void merge_lse_load_at(LA lse_at, int num_splits, int lane, float (&l1)[R]) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) l1[r] = num_splits <= 64 && lane < num_splits ? lp[r][lane * ls_split] : -INFINITY;
+  for (int r = 0; r < R; ++r) l1[r] = num_splits <= 64 && lane < num_splits ? lse_at(r, lane) : -INFINITY;
 }
 
-template <int R, bool ONE = false>
-__device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_t* const* base, int64_t ls_split,
-                                           int64_t os_split, int num_splits, int lane, const float (&l1)[R],
-                                           u32x4 (&out)[R], float (&total)[R]) {
+template <int R, bool ONE, class LA, class OA>
+__device__ __forceinline__ void merge_rows_at(LA lse_at, OA o_at, int num_splits, int lane, const float (&l1)[R],
+                                              u32x4 (&out)[R], float (&total)[R]) {
   float m[R], s[R], acc[R][8];
   const bool one_pass = ONE || num_splits <= 64;
 #pragma unroll
@@ -66,7 +67,7 @@ __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_
   if (!one_pass) {
     for (int k = lane; k < num_splits; k += 64) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) m[r] = nan_max(m[r], lp[r][k * ls_split]);
+      for (int r = 0; r < R; ++r) m[r] = nan_max(m[r], lse_at(r, k));
     }
   }
 #pragma unroll
@@ -77,7 +78,7 @@ __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_
   for (int k = lane; k < num_splits; k += 64) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float l = one_pass ? l1[r] : lp[r][k * ls_split];
+      const float l = one_pass ? l1[r] : lse_at(r, k);
       if (l != -INFINITY) s[r] += expf(l - m[r]);
     }
   }
@@ -95,7 +96,7 @@ __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_
     uint64_t live[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float l = one_pass ? l1[r] : (k < num_splits ? lp[r][k * ls_split] : -INFINITY);
+      const float l = one_pass ? l1[r] : (k < num_splits ? lse_at(r, k) : -INFINITY);
       w[r] = expf(l - total[r]);  // NaN if poisoned (a live split's weight)
       live[r] = __ballot(l != -INFINITY);
     }
@@ -117,7 +118,7 @@ __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (ks[r][j] >= 0) v[r][j] = *reinterpret_cast<const u32x4*>(base[r] + (int64_t)(k0 + ks[r][j]) * os_split);
+          if (ks[r][j] >= 0) v[r][j] = o_at(r, k0 + ks[r][j]);
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -139,6 +140,22 @@ __device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[r][e] = pack_bf16x2(acc[r][2 * e], acc[r][2 * e + 1]);
+}
+
+template <int R>
+__device__ __forceinline__ void merge_lse_load(const float* const* lp, int64_t ls_split, int num_splits, int lane,
+                                               float (&l1)[R]) {
+  merge_lse_load_at<R>([&](int r, int k) { return lp[r][k * ls_split]; }, num_splits, lane, l1);
+}
+
+template <int R, bool ONE = false>
+__device__ __forceinline__ void merge_rows(const float* const* lp, const uint16_t* const* base, int64_t ls_split,
+                                           int64_t os_split, int num_splits, int lane, const float (&l1)[R],
+                                           u32x4 (&out)[R], float (&total)[R]) {
+  merge_rows_at<R, ONE>([&](int r, int k) { return lp[r][k * ls_split]; },
+                        [&](int r, int k) { return *reinterpret_cast<const u32x4*>(base[r] + (int64_t)k * os_split); },
+                        num_splits, lane, l1, out,
+                        total);
 }
 
 // W_UV fragments of all 16 K-steps for output row v of head h: lane group lg

@@ -5,7 +5,9 @@ Variants of the same step: `use_fp8_query(q_scale)` quantises the bf16
 query with concat_quant_fp8 each step and attends on the fp8 codes
 (decode_partial with q_scale); `fused_post = True` runs merge_value_gate in
 place of merge_lse + value_gate (the value heads must be the attention
-heads).  The partials come from the *_hostplan entry points (the split
+heads); `fused_attend = True` runs decode_attend (the partials and their
+merge in one launch, into self.latent) in place of decode_partial +
+merge_lse.  The partials come from the *_hostplan entry points (the split
 partition built on the host from the request offsets) unless `host_plan` is
 set to False, which calls mla_decode_partial(_fp8q); the two give the same
 bits.
@@ -19,8 +21,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (D_LATENT, D_QK, D_V, concat_quant_fp8, decode_partial, kv_write, merge_lse, merge_value_gate,
-               value_gate)
+from . import (D_LATENT, D_QK, D_V, concat_quant_fp8, decode_attend, decode_attend_workspace_bytes, decode_partial,
+               kv_write, merge_lse, merge_value_gate, value_gate)
 from .synth import FP8_NAN, Workload
 
 
@@ -43,6 +45,9 @@ class DeviceStep:
         # run() merges and projects in one call (possible when the value heads
         # are the attention heads); off: mla_merge_lse, then mla_value_gate
         self.fused_post = False
+        # run() attends and merges in one launch (decode_attend, bf16 query)
+        self.fused_attend = False
+        self.workspace = None  # decode_attend's workspace, allocated (zeroed) on first use
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
         self.indptr_host = np.ascontiguousarray(w.indptr, dtype=np.int32)  # the same offsets, on the host
@@ -96,6 +101,18 @@ class DeviceStep:
                        num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale,
                        kv_indptr_host=plan)
 
+    def attend_merged(self):
+        """The partials and their LSE merge in one launch: self.latent (the
+        attention heads) and self.lse, as attend() + merge() give them."""
+        w = self.w
+        if self.workspace is None:
+            n = decode_attend_workspace_bytes(w.batch, w.qlen, w.heads, self.num_workers)
+            self.workspace = torch.zeros(n, dtype=torch.uint8, device=self.dev)
+        decode_attend(self.q, self.kv_cache, self.indptr, self.indices, self.latent[:, :w.heads], self.lse,
+                      self.workspace, self.indptr_host, qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale,
+                      kv_scale=w.kv_scale, num_splits=w.num_splits, num_workers=self.num_workers,
+                      split_min_tokens=self.split_min)
+
     def merge(self):
         merge_lse(self.o_part, self.lse_part, self.latent[:, :self.w.heads], self.lse)
 
@@ -119,6 +136,12 @@ class DeviceStep:
             self.write_new_tokens()
         if self.q_bf16 is not None:
             self.quantize_query()
+        if self.fused_attend:
+            if self.q_scale is not None:
+                raise ValueError("decode_attend takes a bf16 query")
+            self.attend_merged()
+            self.value()
+            return
         self.attend()
         if self.fused_post:
             self.merge_value()
