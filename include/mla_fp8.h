@@ -18,6 +18,7 @@
  *                       above with the split partition computed on the host
  *   mla_decode_attend   the attention and the LSE merge in one launch ->
  *                       latent (bf16) and LSE, with a caller's workspace
+ *   mla_decode_attend_noalloc  the same with the library's own workspace
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
  *   mla_merge_value_gate  the merge, W_UV and gate in one call (no latent written)
@@ -313,6 +314,28 @@ int mla_decode_attend(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_
  * Host only; it depends on the sizes alone (not on the request lengths).
  */
 int64_t mla_decode_attend_workspace_bytes(int32_t batch, int32_t qlen, int32_t heads, int32_t num_workers);
+
+/*
+ * mla_decode_attend for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same call, outputs and errors, without the workspace
+ * arguments.  The workspace is an array of MLA_ATTEND_NOALLOC_MAX_BYTES in
+ * the library's own device memory, one per GPU, held until the process ends;
+ * the first call on a device takes its address there.  The call allocates
+ * nothing and never synchronizes.  Sizes whose workspace
+ * (mla_decode_attend_workspace_bytes) exceeds MLA_ATTEND_NOALLOC_MAX_BYTES
+ * give MLA_ERR_UNSUPPORTED; a failed device query gives MLA_ERR_HIP.  The
+ * array starts zeroed and every completed call leaves its counters zero
+ * again; all calls on one GPU share it, so calls that overlap on one GPU
+ * (different streams, concurrent host threads) race.
+ */
+#define MLA_ATTEND_NOALLOC_MAX_BYTES (32 << 20)
+int mla_decode_attend_noalloc(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head, int32_t batch,
+                              int32_t qlen, int32_t heads, const uint8_t* kv_cache, int64_t num_slots,
+                              const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float kv_scale,
+                              int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                              const int32_t* kv_indptr_host, uint16_t* o, int64_t o_row, int64_t o_head,
+                              float* lse, int64_t l_row, int64_t l_head, void* stream);
 
 /*
  * Host helper: the split partition mla_decode_partial uses.

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
         L.mla_decode_attend.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32, i32, P, P, i64,
                                         i64, P, i64, i64, P, i64, P]
+        L.mla_decode_attend_noalloc.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32, i32, P, P,
+                                                i64, i64, P, i64, i64, P]
         L.mla_decode_attend_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.mla_decode_attend_workspace_bytes.restype = ctypes.c_int64
         L.mla_merge_lse.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, i32, P, i64, i64, P,
@@ -68,7 +70,7 @@ def lib() -> ctypes.CDLL:
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
                      "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate",
-                     "mla_decode_attend"):
+                     "mla_decode_attend", "mla_decode_attend_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -259,6 +261,19 @@ def decode_attend(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tens
         raise MlaError("workspace must be a contiguous uint8 tensor")
     st = lib().mla_decode_attend(*args, _dev(workspace, "workspace", _U8), workspace.numel(), _stream())
     _check(st, "mla_decode_attend")
+
+
+def decode_attend_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,
+                          kv_indices: torch.Tensor, o: torch.Tensor, lse: torch.Tensor | None,
+                          kv_indptr_host: np.ndarray, *, qlen: int, heads: int, sm_scale: float, kv_scale: float,
+                          num_splits: int, num_workers: int = 256, split_min_tokens: int = 256) -> None:
+    """mla_decode_attend_noalloc: decode_attend on the library's own
+    workspace (for callers that cannot allocate); same outputs."""
+    args, ih = _attend_args(q, kv_cache, kv_indptr, kv_indices, o, lse, qlen=qlen, heads=heads, sm_scale=sm_scale,
+                            kv_scale=kv_scale, num_splits=num_splits, num_workers=num_workers,
+                            split_min_tokens=split_min_tokens, kv_indptr_host=kv_indptr_host)
+    st = lib().mla_decode_attend_noalloc(*args, _stream())
+    _check(st, "mla_decode_attend_noalloc")
 
 
 def split_plan(kv_indptr, num_splits: int, num_workers: int, split_min_tokens: int):

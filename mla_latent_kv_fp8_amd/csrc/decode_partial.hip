@@ -41,6 +41,8 @@
 //    goes straight to the merged latent; the pieces of a split request go to
 //    workspace slots, and the block that completes a request's count (a
 //    system-scope atomic) merges its splits with the LSE merge's own code.
+#include <mutex>
+
 #include "post_common.hpp"
 
 namespace mla {
@@ -1244,6 +1246,29 @@ static int attend_impl(const uint16_t* q, int64_t q_stride_row, int64_t q_stride
   }
 }
 
+// The no-allocation call's workspace: one array per GPU in the library's
+// device memory.  Its device address is taken once per device, with that
+// device current, at the first call there; kernels only ever see that
+// address (the array's name is a host-side stand-in).
+static __device__ __align__(256) uint8_t scratch[MLA_ATTEND_NOALLOC_MAX_BYTES];
+constexpr int MAX_DEVICES = 64;
+static void* g_scratch[MAX_DEVICES];
+static std::mutex g_scratch_mu;
+
+static int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MLA_ERR_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MLA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MLA_OK;
+}
+
 }  // namespace mla
 
 extern "C" int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
@@ -1321,3 +1346,21 @@ extern "C" int mla_decode_attend(const uint16_t* q, int64_t q_stride_row, int64_
                           o, o_row, o_head, lse, l_row, l_head, workspace, workspace_bytes, stream);
 }
 
+extern "C" int mla_decode_attend_noalloc(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
+                                         int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,
+                                         int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices,
+                                         float sm_scale, float kv_scale, int32_t num_splits, int32_t num_workers,
+                                         int32_t split_min_tokens, const int32_t* kv_indptr_host, uint16_t* o,
+                                         int64_t o_row, int64_t o_head, float* lse, int64_t l_row, int64_t l_head,
+                                         void* stream) {
+  if (batch < 0 || qlen < 1 || heads < 1 || num_workers < 1) return MLA_ERR_INVALID;
+  if (batch == 0) return MLA_OK;
+  if (mla::attend_layout(batch, qlen, heads, num_workers).total > MLA_ATTEND_NOALLOC_MAX_BYTES)
+    return MLA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const int st = mla::scratch_address(&ws);
+  if (st != MLA_OK) return st;
+  return mla::attend_impl(q, q_stride_row, q_stride_head, batch, qlen, heads, kv_cache, num_slots, kv_indptr,
+                          kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens, kv_indptr_host,
+                          o, o_row, o_head, lse, l_row, l_head, ws, MLA_ATTEND_NOALLOC_MAX_BYTES, stream);
+}
