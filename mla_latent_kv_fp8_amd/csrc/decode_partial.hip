@@ -20,7 +20,10 @@
 //    piece into accumulation registers (the 48-row block too: its whole
 //    query, 216 registers, with O in 96 arch registers).  Wave
 //    w owns token quarter w of every tile for all row groups, so each staged
-//    byte is converted to bf16 once per block.
+//    byte is converted to bf16 once per block.  An fp8 query skips the
+//    conversion: its QK runs on the scaled 16x16x128 fp8 MFMA with K and Q
+//    both E4M3 codes (exact products, f32 sums), q_scale in the score
+//    constant.
 //  * Softmax: base-2, P = 2^(s*c - ref) in bf16, sums in f32, with a
 //    per-row reference ref that starts at 0.  Each lane keeps the running
 //    maximum of its scores; at the end of a piece the four quarters' row
@@ -42,6 +45,7 @@
 //    workspace slots, and the block that completes a request's count (a
 //    system-scope atomic) merges its splits with the LSE merge's own code.
 #include <mutex>
+#include <type_traits>
 
 #include "post_common.hpp"
 
@@ -282,25 +286,28 @@ __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, const int64
   return n;
 }
 
-// The staged query -> this wave's bf16 query fragments qf[g][s] (K-step s
-// of row group g).  An fp8 query is decoded exactly (E4M3 fits in bf16);
-// q_scale is folded into the score constant.
-template <int NRG, bool QF8>
+// The fp8 query's QK runs on the fp8 MFMA: its fragments stay E4M3 codes,
+// 16 bytes per 64-dim group pp (dims 64pp + 16lg .. +15), the same bytes
+// the K chunk of that group holds for the token; q_scale is folded into the
+// score constant.
+template <int NRG>
+__device__ __forceinline__ void read_q(MLA_LDS uint8_t* buf2, MLA_LDS uint8_t* qarea, int lane,
+                                       u32x4 (&qf)[NRG][9]) {
+#pragma unroll
+  for (int g = 0; g < NRG; ++g)
+#pragma unroll
+    for (int pp = 0; pp < 9; ++pp) qf[g][pp] = *(const MLA_LDS u32x4*)(q_block(buf2, qarea, 9 * g + pp) + 16 * lane);
+}
+
+// The staged bf16 query -> this wave's query fragments qf[g][s] (K-step s
+// of row group g).
+template <int NRG>
 __device__ __forceinline__ void read_q(MLA_LDS uint8_t* buf2, MLA_LDS uint8_t* qarea, int lane,
                                        bf16x8 (&qf)[NRG][18]) {
 #pragma unroll
   for (int g = 0; g < NRG; ++g)
 #pragma unroll
-    for (int pp = 0; pp < 9; ++pp) {
-      if constexpr (QF8) {
-        const u32x4 raw = *(const MLA_LDS u32x4*)(q_block(buf2, qarea, 9 * g + pp) + 16 * lane);
-        qf[g][2 * pp] = fp8x8_to_bf16x8(u32x2{raw[0], raw[1]});
-        qf[g][2 * pp + 1] = fp8x8_to_bf16x8(u32x2{raw[2], raw[3]});
-      } else {
-        qf[g][2 * pp] = *(const MLA_LDS bf16x8*)(q_block(buf2, qarea, 18 * g + 2 * pp) + 16 * lane);
-        qf[g][2 * pp + 1] = *(const MLA_LDS bf16x8*)(q_block(buf2, qarea, 18 * g + 2 * pp + 1) + 16 * lane);
-      }
-    }
+    for (int s = 0; s < 18; ++s) qf[g][s] = *(const MLA_LDS bf16x8*)(q_block(buf2, qarea, 18 * g + s) + 16 * lane);
 }
 
 // A valid cache row among the first n staged indices (0 if there is none),
@@ -442,6 +449,46 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
     khi = nhi;
     interleave<2 * NRG, 8, 1>();
     __builtin_amdgcn_sched_barrier(0);  // keep the steps (and their read-ahead) in order
+  }
+}
+
+// QK of one tile for an fp8 query, on the fp8 MFMA straight from the
+// staged E4M3 bytes (no conversion of K): the 576 dims as four 128-dim
+// steps, step s taking 64-dim groups 2s and 2s+1 (the chunk lane group lg
+// reads from each, 32 bytes per lane; the query fragment holds the same
+// dims), then the 64 rope dims as two 32-dim steps on the halves of group
+// 8's chunk.  Operand and accumulator layouts as in qk_tile; the products
+// are exact and accumulate in f32.
+template <int NRG>
+__device__ __forceinline__ void qk_tile_f8(const MLA_LDS uint8_t* kt, const u32x4 (&qf)[NRG][9], int wave, int lane,
+                                           f32x4 (&S)[NRG]) {
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
+  const MLA_LDS uint8_t* kq = kt + tile_off(16 * wave + lr, lg);
+  u32x4 raw[9];
+#pragma unroll
+  for (int pp = 0; pp < 9; ++pp) raw[pp] = *(const MLA_LDS u32x4*)(kq + 1024 * pp);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const i32x8 a = __builtin_bit_cast(i32x8, u32x8{raw[2 * st][0], raw[2 * st][1], raw[2 * st][2], raw[2 * st][3],
+                                                    raw[2 * st + 1][0], raw[2 * st + 1][1], raw[2 * st + 1][2],
+                                                    raw[2 * st + 1][3]});
+#pragma unroll
+    for (int g = 0; g < NRG; ++g) {
+      const u32x4 q0 = qf[g][2 * st], q1 = qf[g][2 * st + 1];
+      const i32x8 bq = __builtin_bit_cast(i32x8, u32x8{q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]});
+      // E4M3 operands (format 0), unit E8M0 scales (127)
+      S[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, S[g], 0, 0, 0, 127, 0, 127);
+    }
+  }
+  const long alo = (long)(((uint64_t)raw[8][1] << 32) | raw[8][0]);
+  const long ahi = (long)(((uint64_t)raw[8][3] << 32) | raw[8][2]);
+#pragma unroll
+  for (int g = 0; g < NRG; ++g) {
+    const u32x4 q8 = qf[g][8];
+    S[g] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(alo, (long)(((uint64_t)q8[1] << 32) | q8[0]), S[g], 0, 0, 0);
+    S[g] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ahi, (long)(((uint64_t)q8[3] << 32) | q8[2]), S[g], 0, 0, 0);
   }
 }
 
@@ -733,12 +780,12 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // the query fragments: K-step 2pp uses dims 64pp+16lg..+7, 2pp+1 the
     // next 8 (the K fragments use the same order); kept in AGPRs (they are
     // only MFMA B operands), so the arch VGPRs hold the per-tile working set
-    bf16x8 qf[NRG][18];
-    read_q<NRG, QF8>(kbuf + 2 * TILE_BYTES, qarea, lane, qf);
+    typename std::conditional<QF8, u32x4[NRG][9], bf16x8[NRG][18]>::type qf;
+    read_q<NRG>(kbuf + 2 * TILE_BYTES, qarea, lane, qf);
 #pragma unroll
     for (int g = 0; g < NRG; ++g)
 #pragma unroll
-      for (int ss = 0; ss < 18; ++ss) asm volatile("" : "+a"(qf[g][ss]));
+      for (int ss = 0; ss < (QF8 ? 9 : 18); ++ss) asm volatile("" : "+a"(qf[g][ss]));
 
     f32x4 O[8][NRG];
     // per row: the softmax reference (log2 units) and its negation, the
@@ -805,7 +852,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
         const int nrow = it + 2 < ntiles ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
         f32x4 S[NRG];
-        qk_tile<NRG>(kt, qf, wave, lane, S);
+        if constexpr (QF8)
+          qk_tile_f8<NRG>(kt, qf, wave, lane, S);
+        else
+          qk_tile<NRG>(kt, qf, wave, lane, S);
         // ---- mask (raw score units) only where a row's visible range or a
         // bad index reaches into this quarter
         {

@@ -228,13 +228,19 @@ def test_fp8_query_parity_small(ops, oracle, name, batch, lr, nw, smin, q_scale)
 @pytest.mark.parametrize("heads", [16, 32, 96])
 def test_fp8_query_power_of_two_scale_is_the_bf16_query(ops, heads, monkeypatch):
     """With q_scale = 2^-4 every decoded query element q_scale * fp8(code) is
-    exactly a bf16 value, and every score of the two entry points differs by
-    an exact power of two that the score constant undoes: the fp8-query
-    partials must equal the bf16-query partials bit for bit."""
+    exactly a bf16 value, so the two entry points see the same exact
+    products.  The fp8-query call forms each score on the scaled fp8 MFMA
+    (128 products per instruction) and the bf16 call on the bf16 MFMA (32 per
+    instruction): only the order of the f32 additions differs, and a score
+    that moves in its last bits can round its bf16 P to the neighbouring
+    value, which moves O by an absolute amount.  The partial LSE must agree
+    to 1e-4 (f32 sums of 576 products; measured <= 1e-5), O within the
+    tolerance the oracle tests use, and at least 90% of the O elements bit
+    for bit (measured 97%); the empty-split pattern must be the same."""
     from mla_latent_kv_fp8_amd import synth
     from mla_latent_kv_fp8_amd.step import DeviceStep
 
-    _announce(f"fp8 query == bf16 query bitwise ({heads} heads)")
+    _announce(f"fp8 query vs bf16 query at q_scale 2^-4 ({heads} heads)")
     spec = dict(synth.SPECS["batch"], heads=heads, heads_pad=128 if heads == 96 else heads)
     monkeypatch.setitem(synth.SPECS, "batch", spec)
     w = synth.make("batch", batch=4, len_range=(50, 900))
@@ -248,17 +254,23 @@ def test_fp8_query_power_of_two_scale_is_the_bf16_query(ops, heads, monkeypatch)
     a.attend()
     b.attend()
     torch.cuda.synchronize()
-    assert torch.equal(a.lse_part, b.lse_part)
-    fin = torch.isfinite(a.lse_part)
-    assert torch.equal(a.o_part.view(torch.int16)[fin], b.o_part.view(torch.int16)[fin])
+    la, lb = a.lse_part.cpu().numpy(), b.lse_part.cpu().numpy()
+    fin = np.isfinite(lb)
+    assert np.array_equal(np.isfinite(la), fin) and np.array_equal(np.isneginf(la), np.isneginf(lb))
+    assert np.abs(la[fin].astype(np.float64) - lb[fin]).max(initial=0) <= 1e-4
+    oa, ob = _np_bf16(a.o_part)[fin], _np_bf16(b.o_part)[fin]
+    fa = (oa.astype(np.uint32) << 16).view(np.float32)
+    fb = (ob.astype(np.uint32) << 16).view(np.float32)
+    assert o_err_ok(fa, fb), np.abs(fa.astype(np.float64) - fb).max(initial=0)
+    assert (oa == ob).mean() >= 0.9
 
 
 @pytest.mark.parametrize("heads", [16, 96])
 def test_fp8_query_restart_on_late_spike(ops, oracle, heads, monkeypatch):
     """fp8 query: a late token aligned with one head's query outgrows the
-    reference by far more than 2^64, so the piece restarts; the decoded
-    query (registers and, for the 48-row block, LDS) must survive the
-    restart.  Exact attention still holds."""
+    reference by far more than 2^64, so the piece restarts; the query codes
+    held in registers must survive the restart.  Exact attention still
+    holds."""
     from mla_latent_kv_fp8_amd import synth
     from mla_latent_kv_fp8_amd.step import DeviceStep
 
