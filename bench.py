@@ -13,12 +13,28 @@ touched from L2 and the 256 MB Infinity Cache, so `value` is a cold-cache,
 HBM-served figure.  The eviction reads rather than writes: a 512 MiB write
 would leave as many dirty lines in the caches, to be written back to HBM
 during the timed step (measured: it halves the rate of a plain gather of the
-same cache rows).  Warm back-to-back numbers are reported alongside.  Prints
-ONE JSON line.
+same cache rows).  Warm back-to-back numbers are reported alongside.
+
+The host must stay ahead of the GPU, or a step's GPU time includes waits
+for its own launches (the Python binding takes about 55 us of host time
+per step, the eviction read only about 70 us of GPU time).  Two things
+broke that and made the slow-step tail (mean several microseconds above the
+median over a short run): the first step of a loop started from an idle
+GPU, and Python's cyclic garbage collector paused the host for up to ~40 ms
+in mid-loop (measured: one pause turned a 200-step warm loop from 82 to 270
+us per step).  So every timed loop starts behind a short spin kernel (about
+0.4 ms) and runs with the collector off (collected once before).
+
+Besides the headline workload, the line carries the partial kernel's
+roofline on the other configurations (a short cold partial-only loop each):
+rank_share against HBM, spec_q8 and long against bf16 MFMA, and the batch
+workload's fp8-query call against the MFMA peak of its mix (QK on the fp8
+MFMA, PV on the bf16 MFMA).  Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -29,6 +45,8 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
+LEAD_CYCLES = 1_000_000  # the spin kernel ahead of a timed loop (about 0.4 ms)
 
 
 def parse():
@@ -45,6 +63,9 @@ def parse():
                     help="merge + W_UV + gate as mla_merge_lse then mla_value_gate (the faster, measured), "
                          "or as one call (mla_merge_value_gate; needs value heads == attention heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-config-rooflines", action="store_true",
+                    help="skip the partial kernel's rooflines on the other configurations")
+    ap.add_argument("--config-iters", type=int, default=20)
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
@@ -78,7 +99,8 @@ def copy_probe():
 
 
 def algorithmic(w):
-    """KV bytes and MFMA flops of the partial kernel per launch."""
+    """KV bytes and MFMA flops of the partial kernel per launch (QK 2*576
+    and PV 2*512 flops per visible (row, token) pair)."""
     L = w.lengths.astype(np.int64)
     kv_bytes = int(L.sum()) * 576
     visible = 0
@@ -86,6 +108,26 @@ def algorithmic(w):
         visible += int(np.maximum(L - w.qlen + j + 1, 0)[L > 0].sum())
     flops = 2176 * w.heads * visible
     return kv_bytes, flops
+
+
+def mixed_peak_tflops():
+    """The MFMA peak of the fp8-query call: its 1152 QK flops per pair on
+    the fp8 MFMA, its 1024 PV flops on the bf16 MFMA."""
+    return 2176.0 / (1152.0 / FP8_MFMA_PEAK_TFLOPS + 1024.0 / BF16_MFMA_PEAK_TFLOPS)
+
+
+def roof_of(flops, kv_bytes, us, mfma_peak):
+    """Both roofs of one partial launch and the one that bounds it (MFMA
+    when its flops per KV byte exceed the chip's balance, else HBM)."""
+    tflops = flops / (us * 1e-6) / 1e12
+    gbs = kv_bytes / (us * 1e-6) / 1e9
+    mfma = {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(mfma_peak, 1), "unit": "TFLOP/s",
+            "frac": round(tflops / mfma_peak, 4)}
+    hbm = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if flops / max(kv_bytes, 1) > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        return mfma, hbm
+    return hbm, mfma
 
 
 def step_bytes(w, num_workers, split_min):
@@ -142,6 +184,63 @@ def measured_traffic(config):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def host_cpu():
+    """The host's CPU model and its logical CPU count, from /proc/cpuinfo."""
+    model, n = "unknown", 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name") and model == "unknown":
+                    model = line.split(":", 1)[1].strip()
+                elif line.startswith("processor"):
+                    n += 1
+    except OSError:
+        pass
+    return "%s (%d logical CPUs visible; %d usable by this process)" % (model, n, len(os.sched_getaffinity(0)))
+
+
+def config_roofline(torch, evict, name, fp8_query, iters):
+    """The partial kernel's cold roofline on one more configuration: a short
+    partial-only loop, each launch after the eviction read, with its own
+    events."""
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    w = synth.make(name)
+    print("[bench] partial roofline on %s%s: B=%d qlen=%d H=%d tokens=%d" %
+          (name, " (fp8 query)" if fp8_query else "", w.batch, w.qlen, w.heads, w.total_tokens),
+          file=sys.stderr, flush=True)
+    st = DeviceStep(w)
+    if fp8_query:
+        st.use_fp8_query(1.0 / 16.0)
+        st.quantize_query()
+    st.write_new_tokens()
+    for _ in range(3):
+        st.attend()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    gc.collect()
+    gc.disable()
+    torch.cuda._sleep(LEAD_CYCLES)
+    for a, b in ev:
+        evict()
+        a.record()
+        st.attend()
+        b.record()
+    torch.cuda.synchronize()
+    gc.enable()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    kv_bytes, flops = algorithmic(w)
+    roof, other = roof_of(flops, kv_bytes, us, mixed_peak_tflops() if fp8_query else BF16_MFMA_PEAK_TFLOPS)
+    roof.update({"us": round(us, 2), "other": other, "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+                 "workload": "%s: B=%d qlen=%d heads=%d tokens=%d%s" % (name, w.batch, w.qlen, w.heads,
+                                                                        w.total_tokens,
+                                                                        ", fp8 query" if fp8_query else "")})
+    del st
+    torch.cuda.empty_cache()
+    return roof
+
+
 def cpu_baseline(w, budget_s):
     """The oracle (as it stands) on a bounded sample of the same workload:
     the first requests of the batch until about `budget_s` of CPU work."""
@@ -175,7 +274,7 @@ def cpu_baseline(w, budget_s):
         if t_total >= budget_s:
             break
     return {"value": round(done_bytes / t_total / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": host_cpu(),
             "sample": "%d of %d requests of the workload (all %d heads, whole contexts, %d KV tokens): "
                       "cache write + exact attention + W_UV/gate, %.1f s" %
                       (n_req, w.batch, H, done_bytes // 576, t_total)}
@@ -205,13 +304,16 @@ def main():
         # the runtime's fp8 path: each step quantises the bf16 query (q_scale
         # 1/16 for the N(0,1) synthetic query), then attends on the fp8 codes
         st.use_fp8_query(1.0 / 16.0)
-    st.fused_post = args.post == "fused" and w.value_heads == w.heads
+    st.fused_post = fused_post = args.post == "fused" and w.value_heads == w.heads
     evict = Evict(torch)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
+        evict()
         st.run()
     torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()  # no collector pause inside a timed loop (re-enabled after them)
 
     K = args.steps
     # one event pair per step and none inside it: an event recorded between
@@ -219,6 +321,7 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    torch.cuda._sleep(LEAD_CYCLES)  # the host gets ahead of the GPU before the first step
     for i in range(K):
         evict()  # L2 and Infinity Cache hold nothing of the step (outside its events)
         ev[i][0].record()
@@ -229,6 +332,7 @@ def main():
     step_ms = [a.elapsed_time(b) for a, b in ev]
     # the step's first part (new rows written, query quantised, partials), cold
     ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda._sleep(LEAD_CYCLES)
     for i in range(K):
         evict()
         ea[i][0].record()
@@ -241,6 +345,7 @@ def main():
     attn_ms = [a.elapsed_time(b) for a, b in ea]
     # warm: the same steps back to back
     wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(LEAD_CYCLES)
     wa.record()
     for _ in range(K):
         st.run()
@@ -250,6 +355,7 @@ def main():
 
     # the partial kernel alone (its own events), cold
     pk = []
+    torch.cuda._sleep(LEAD_CYCLES)
     for _ in range(K):
         evict()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -259,12 +365,11 @@ def main():
         pk.append((a, b))
     torch.cuda.synchronize()
     partial_ms = float(np.mean([a.elapsed_time(b) for a, b in pk]))
+    gc.enable()
 
     kv_bytes, flops = algorithmic(w)
     ms = float(np.mean(step_ms))
     value = kv_bytes / (ms * 1e-3) / 1e9
-    tflops = flops / (partial_ms * 1e-3) / 1e12
-    gbs_partial = kv_bytes / (partial_ms * 1e-3) / 1e9
     sb = step_bytes(w, st.num_workers, st.split_min)
     # the partial kernel's bound: MFMA when its flops per KV byte exceed the
     # chip's balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), else HBM
@@ -272,14 +377,19 @@ def main():
     common = {"traffic": traffic, "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
               "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
               "flop_per_byte": round(flops / max(kv_bytes, 1), 1)}
-    mfma_roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                 "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
-    hbm_roof = {"bound": "hbm", "achieved": round(gbs_partial, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs_partial / HBM_PEAK_GBS, 4)}
-    if flops / max(kv_bytes, 1) > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        roof, other_key, other = dict(mfma_roof, **common), "roofline_hbm", hbm_roof
-    else:
-        roof, other_key, other = dict(hbm_roof, **common), "roofline_mfma", mfma_roof
+    roof, other = roof_of(flops, kv_bytes, partial_ms * 1e3,
+                          mixed_peak_tflops() if args.fp8_query else BF16_MFMA_PEAK_TFLOPS)
+    roof = dict(roof, **common)
+    other_key = "roofline_hbm" if roof["bound"] == "mfma" else "roofline_mfma"
+    by_config = None
+    if not args.no_config_rooflines:
+        del st
+        torch.cuda.empty_cache()
+        by_config = {}
+        for name, fq in (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True)):
+            if (name, fq) == (args.config, args.fp8_query):
+                continue
+            by_config[name + ("_fp8_query" if fq else "")] = config_roofline(torch, evict, name, fq, args.config_iters)
     out = {
         "metric": "MLA decode: fp8-KV GB/s + MFMA TFLOP/s vs peak; us/step at B=64, H=128",
         "value": round(value, 2),
@@ -290,23 +400,28 @@ def main():
         "ms_per_step": round(ms, 5),
         "us_per_step": round(ms * 1e3, 2),
         "us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "us_per_step_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+        "us_per_step_max": round(float(np.max(step_ms)) * 1e3, 2),
         "us_per_step_warm": round(warm_ms * 1e3, 2),
         "step_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 KV%s, bf16 MFMA (f32 accumulate)" % (" and query" if args.fp8_query else ""),
+        "dtype": ("fp8-e4m3 KV and query, fp8 MFMA QK + bf16 MFMA PV (f32 accumulate)" if args.fp8_query
+                  else "fp8-e4m3 KV, bf16 MFMA (f32 accumulate)"),
         "data": "synthetic (seeded; no dataset or weights)",
         "config": {"workload": "%s: B=%d qlen=%d heads=%d (query buffer %d%s) tokens=%d kv_scale=%g "
                                "splits<=%d workers=%d W_UV=%s" % (w.name, w.batch, w.qlen, w.heads, w.heads_pad,
                                                                   ", fp8 E4M3 + per-tensor scale" if args.fp8_query
                                                                   else " bf16", w.total_tokens, w.kv_scale,
                                                                   w.num_splits, w.num_workers, w.w_format),
-                   "post": "merge+W_UV+gate fused" if st.fused_post else "merge, then W_UV+gate",
+                   "post": "merge+W_UV+gate fused" if fused_post else "merge, then W_UV+gate",
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
         "roofline": roof,
         # the other roof of the same kernel, for reference
         other_key: other,
+        # the same kernel on the other configurations (cold partial-only loops)
+        "roofline_by_config": by_config,
         "step_bytes": sb,
         "step_gbs_all_bytes": round(sb["total"] / (ms * 1e-3) / 1e9, 1),
         "attend_us_in_step": round(float(np.mean(attn_ms)) * 1e3, 2),
