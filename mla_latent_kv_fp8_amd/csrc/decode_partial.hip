@@ -31,7 +31,10 @@
 //    more than 64 log2 units from its reference takes the maximum as its
 //    reference and the piece runs again (P <= 2^64 then bounds bf16 P and
 //    the f32 sums).  No tile waits for a decision about the reference, and
-//    O is never rescaled.  One barrier per tile publishes P^T.
+//    O is never rescaled.  Two barriers per tile: the first frees the
+//    buffer of tile i-1 for the loads of tile i+2, which issue one per QK
+//    step (so the address unit works through them while the MFMAs run); the
+//    second publishes P^T.
 //  * PV as O^T = V^T . P^T: wave w owns latent columns [128w, 128w+128).
 //    The A operand (8 tokens of one column) comes straight from the
 //    staged tile with ds_read_b64_tr_b8; the B operand is P^T, written to
@@ -189,6 +192,24 @@ __device__ __forceinline__ void issue_tile(const uint8_t* kv, int64_t num_slots,
   const uint32_t d = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + 1024 * 9 * wave));
 #pragma unroll
   for (int cg = 0; cg < 9; ++cg) lds_dma16(src + 64 * cg, d + 1024 * cg);
+}
+
+// The same loads one instruction at a time: tile_dma(...)(cg) fills block
+// (w, cg), so a tile's 9 loads per wave can be spread over other work.
+struct TileDma {
+  const uint8_t* src;
+  uint32_t d;
+  __device__ __forceinline__ void operator()(int cg) const { lds_dma16(src + 64 * cg, d + 1024 * cg); }
+};
+struct NoDma {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+__device__ __forceinline__ TileDma tile_dma(const uint8_t* kv, int64_t num_slots, int row, int safe_row,
+                                            MLA_LDS uint8_t* dst, int wave, int lane) {
+  const int t = 16 * wave + (lane >> 2);
+  row = (uint32_t)row < (uint64_t)num_slots ? row : safe_row;
+  return TileDma{kv + (int64_t)row * MLA_D_QK + 16 * ((lane & 3) ^ hsw(t)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(dst + 1024 * 9 * wave))};
 }
 
 constexpr int IDX_CAP = 2048;  // tokens whose cache indices are staged at once
@@ -420,9 +441,9 @@ __device__ __forceinline__ void pv_tile(const MLA_LDS uint8_t* kt, const uint16_
 // of token 16*wave+lr (block (wave, pp) of the staged tile); K reads run
 // two steps ahead of their conversion, and each step interleaves its MFMAs
 // with the conversions of the next step.
-template <int NRG>
+template <int NRG, typename DMA>
 __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 (&qf)[NRG][18], int wave, int lane,
-                                        f32x4 (&S)[NRG]) {
+                                        f32x4 (&S)[NRG], const DMA& dma) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
@@ -434,6 +455,8 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
   bf16x8 khi = fp8x8_to_bf16x8(u32x2{raw[0][2], raw[0][3]});
 #pragma unroll
   for (int pp = 0; pp < 9; ++pp) {
+    if (pp == 0) { dma(0); dma(1); dma(2); }
+    if (pp >= 1 && pp <= 3) { dma(2 * pp + 1); dma(2 * pp + 2); }
     if (pp + 2 < 9) raw[(pp + 2) % 3] = *(const MLA_LDS u32x4*)(kq + 1024 * (pp + 2));
     bf16x8 nlo = klo, nhi = khi;
     if (pp + 1 < 9) {
@@ -456,12 +479,12 @@ __device__ __forceinline__ void qk_tile(const MLA_LDS uint8_t* kt, const bf16x8 
 // staged E4M3 bytes (no conversion of K): the 576 dims as four 128-dim
 // steps, step s taking 64-dim groups 2s and 2s+1 (the chunk lane group lg
 // reads from each, 32 bytes per lane; the query fragment holds the same
-// dims), then the 64 rope dims as two 32-dim steps on the halves of group
-// 8's chunk.  Operand and accumulator layouts as in qk_tile; the products
-// are exact and accumulate in f32.
-template <int NRG>
+// dims), then the 64 rope dims as a fifth step whose other half is zero.
+// Operand and accumulator layouts as in qk_tile; the products are exact and
+// accumulate in f32.
+template <int NRG, typename DMA>
 __device__ __forceinline__ void qk_tile_f8(const MLA_LDS uint8_t* kt, const u32x4 (&qf)[NRG][9], int wave, int lane,
-                                           f32x4 (&S)[NRG]) {
+                                           f32x4 (&S)[NRG], const DMA& dma) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
   for (int g = 0; g < NRG; ++g) S[g] = f32x4{0, 0, 0, 0};
@@ -471,6 +494,8 @@ __device__ __forceinline__ void qk_tile_f8(const MLA_LDS uint8_t* kt, const u32x
   for (int pp = 0; pp < 9; ++pp) raw[pp] = *(const MLA_LDS u32x4*)(kq + 1024 * pp);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
+    dma(2 * st);
+    dma(2 * st + 1);
     const i32x8 a = __builtin_bit_cast(i32x8, u32x8{raw[2 * st][0], raw[2 * st][1], raw[2 * st][2], raw[2 * st][3],
                                                     raw[2 * st + 1][0], raw[2 * st + 1][1], raw[2 * st + 1][2],
                                                     raw[2 * st + 1][3]});
@@ -481,14 +506,17 @@ __device__ __forceinline__ void qk_tile_f8(const MLA_LDS uint8_t* kt, const u32x
       // E4M3 operands (format 0), unit E8M0 scales (127)
       S[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, bq, S[g], 0, 0, 0, 127, 0, 127);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  const long alo = (long)(((uint64_t)raw[8][1] << 32) | raw[8][0]);
-  const long ahi = (long)(((uint64_t)raw[8][3] << 32) | raw[8][2]);
+  dma(8);
+  // the rope dims: group 8's chunk in the low 16 bytes of both operands,
+  // zeros in the high 16 (one MFMA type along the whole accumulation chain)
+  const i32x8 ar = __builtin_bit_cast(i32x8, u32x8{raw[8][0], raw[8][1], raw[8][2], raw[8][3], 0u, 0u, 0u, 0u});
 #pragma unroll
   for (int g = 0; g < NRG; ++g) {
     const u32x4 q8 = qf[g][8];
-    S[g] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(alo, (long)(((uint64_t)q8[1] << 32) | q8[0]), S[g], 0, 0, 0);
-    S[g] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ahi, (long)(((uint64_t)q8[3] << 32) | q8[2]), S[g], 0, 0, 0);
+    const i32x8 bq = __builtin_bit_cast(i32x8, u32x8{q8[0], q8[1], q8[2], q8[3], 0u, 0u, 0u, 0u});
+    S[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ar, bq, S[g], 0, 0, 0, 127, 0, 127);
   }
 }
 
@@ -843,19 +871,33 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         __syncthreads();
       }
 
-      // One barrier per tile: it publishes P^T of tile it and tile it+1.
+      // P^T is double buffered by tile parity.
       for (int it = 0; it < ntiles; ++it) {
         const int t0 = s0 + NT * it;
         const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
         uint16_t* ptb = pt + (it & 1) * PT_ELEMS;
         // indices for this tile's mask and tile it+2's loads, read ahead of QK
         const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
-        const int nrow = it + 2 < ntiles ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
+        const bool more = it + 2 < ntiles;
+        const int nrow = more ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
+        // every wave is past PV of tile it-1 (and, at the first tile, past
+        // its query reads): that buffer takes tile it+2, whose loads issue
+        // one per QK step
+        __syncthreads();
         f32x4 S[NRG];
-        if constexpr (QF8)
-          qk_tile_f8<NRG>(kt, qf, wave, lane, S);
-        else
-          qk_tile<NRG>(kt, qf, wave, lane, S);
+        if (more) {
+          const TileDma dma =
+              tile_dma(p.kv, p.num_slots, nrow, safe_row, kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+          if constexpr (QF8)
+            qk_tile_f8<NRG>(kt, qf, wave, lane, S, dma);
+          else
+            qk_tile<NRG>(kt, qf, wave, lane, S, dma);
+        } else {
+          if constexpr (QF8)
+            qk_tile_f8<NRG>(kt, qf, wave, lane, S, NoDma{});
+          else
+            qk_tile<NRG>(kt, qf, wave, lane, S, NoDma{});
+        }
         // ---- mask (raw score units) only where a row's visible range or a
         // bad index reaches into this quarter
         {
@@ -883,10 +925,12 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
         i32x2 v0[8];
         read_v(kt, 0, vo, v0);               // in flight across the barrier
-        if (it + 1 < ntiles) wait_vm_all();  // tile it+1 has landed (this wave's part)
-        __syncthreads();                     // P^T of tile it; tile it+1 visible
-        if (it + 2 < ntiles)
-          issue_tile(p.kv, p.num_slots, nrow, safe_row, kbuf + ((it + 2) % NBUF) * TILE_BYTES, wave, lane);
+        // tile it+1 has landed (this wave's part; tile it+2's 9 loads may fly)
+        if (more)
+          asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else if (it + 1 < ntiles)
+          wait_vm_all();
+        __syncthreads();  // P^T of tile it; tile it+1 visible
 #pragma unroll
         for (int g = 0; g < NRG; ++g) lsum[g] += ps[g];
         pv_tile<NRG>(kt, ptb, O, v0, vo, lane);
