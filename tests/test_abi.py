@@ -152,6 +152,31 @@ def test_bench_step_bytes_counts_live_splits():
     assert sb["total"] == sum(v for k, v in sb.items() if k != "total")
 
 
+def test_bench_roofline_bound_and_mixed_peak():
+    # the bound of a partial launch follows its flop per KV byte against the
+    # chip's balance for the MFMA peak in play; the fp8-query call's peak is
+    # the harmonic mix of its QK flops on the fp8 MFMA and its PV flops on
+    # the bf16 MFMA (2176 / (1152 / 5000 + 1024 / 2500) = 3400 TFLOP/s)
+    import bench
+
+    assert abs(bench.mixed_peak_tflops() - 3400.0) < 1e-9
+    # batch-like: 363 flop/B > 312.5 -> MFMA-bound against bf16, HBM-bound against the mix (425)
+    roof, other = bench.roof_of(53.16e9, 146.59e6, 70.0, bench.BF16_MFMA_PEAK_TFLOPS)
+    assert roof["bound"] == "mfma" and other["bound"] == "hbm"
+    assert abs(roof["achieved"] - 53.16e9 / 70e-6 / 1e12) < 0.01
+    assert abs(roof["frac"] - roof["achieved"] / 2500.0) < 1e-4
+    roof, other = bench.roof_of(53.16e9, 146.59e6, 70.0, bench.mixed_peak_tflops())
+    assert roof["bound"] == "hbm" and other["bound"] == "mfma"
+    assert abs(roof["achieved"] - 146.59e6 / 70e-6 / 1e9) < 0.1
+
+
+def test_bench_host_cpu_names_the_model():
+    import bench
+
+    h = bench.host_cpu()
+    assert "logical CPUs visible" in h and "usable by this process" in h
+
+
 def test_hostplan_argument_errors(mlib):
     # the host-plan entry point: a null host copy of the offsets, or a
     # decreasing one, is rejected before anything is enqueued
