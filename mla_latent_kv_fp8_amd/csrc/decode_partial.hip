@@ -243,6 +243,24 @@ __device__ __forceinline__ int wave_min64(int x) {
   return __builtin_amdgcn_readfirstlane(min((int)b[0], (int)b[1]));
 }
 
+// max(a, b, c) on one v_max3_f32.  Every score here is a number or a quiet
+// NaN (MFMA results, the mask's NaN), and a quiet NaN operand is passed
+// over, so this is fmaxf(a, fmaxf(b, c)) without the compiler's
+// signaling-NaN quieting of each operand.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Whether any of the first n staged cache indices in this wave's share
+// (entries 64*wave + lane, stepping by 256) lies outside [0, num_slots).
+__device__ __forceinline__ bool idx_share_bad(const MLA_LDS int32_t* idx, int n, uint32_t ns, int wave, int lane) {
+  bool bad = false;
+  for (int i = 64 * wave + lane; i < n; i += 256) bad |= (uint32_t)idx[i] >= ns;
+  return __any(bad);
+}
+
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
@@ -549,6 +567,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   __shared__ __attribute__((aligned(16))) int32_t idx[IDX_CAP];
   __shared__ __attribute__((aligned(16))) uint8_t qarea_[q_area_bytes<NRG, QF8>()];  // query staging, past tile buffer 2
   __shared__ int32_t red_i[4];
+  __shared__ int32_t segbad_[4];  // per wave: a bad cache index in its share of the segment
   __shared__ int64_t rowoff[RB];  // output offset of block row i within its request, -1 past M
   __shared__ int64_t latoff[FUSE ? RB : 1];  // the same in the merged latent
   __shared__ int32_t last_[1];               // fused call: the counter value this block saw
@@ -797,6 +816,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       if (slen > NT)
         issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
                    kbuf + TILE_BYTES, wave, lane);
+      {
+        const bool bad = idx_share_bad(idxl, slen, (uint32_t)p.num_slots, wave, lane);
+        if (lane == 0) segbad_[wave] = bad;  // read after the barrier below
+      }
       // the query (issued before the tiles) and tile 0 have landed; tile 1's
       // 9 loads may still fly
       if (slen > NT)
@@ -864,6 +887,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         if (ntiles > 1)
           issue_tile(p.kv, p.num_slots, tile_row(idxl + NT, min(NT, slen - NT), wave, lane), safe_row,
                      kbuf + TILE_BYTES, wave, lane);
+        {
+          const bool bad = idx_share_bad(idxl, slen, (uint32_t)p.num_slots, wave, lane);
+          if (lane == 0) segbad_[wave] = bad;  // read after the barrier below
+        }
         if (ntiles > 1)
           asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // tile 0's 9 loads (tile 1's may fly)
         else
@@ -871,13 +898,16 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         __syncthreads();
       }
 
+      // a bad cache index anywhere in this segment sends every tile through
+      // the masking path (which then finds it); written before the barrier
+      // that follows tile 0's wait
+      const bool seg_bad = (segbad_[0] | segbad_[1] | segbad_[2] | segbad_[3]) != 0;
       // P^T is double buffered by tile parity.
       for (int it = 0; it < ntiles; ++it) {
         const int t0 = s0 + NT * it;
         const MLA_LDS uint8_t* kt = kbuf + (it % NBUF) * TILE_BYTES;
         uint16_t* ptb = pt + (it & 1) * PT_ELEMS;
-        // indices for this tile's mask and tile it+2's loads, read ahead of QK
-        const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
+        // tile it+2's rows, read ahead of QK
         const bool more = it + 2 < ntiles;
         const int nrow = more ? tile_row(idxl + NT * (it + 2), min(NT, slen - NT * (it + 2)), wave, lane) : 0;
         // every wave is past PV of tile it-1 (and, at the first tile, past
@@ -902,11 +932,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         // bad index reaches into this quarter
         {
           const int tq0 = t0 + 16 * wave;
-          const uint32_t ns = (uint32_t)p.num_slots;
-          const bool bad0 = (uint32_t)ids[0] >= ns, bad1 = (uint32_t)ids[1] >= ns;
-          const bool bad2 = (uint32_t)ids[2] >= ns, bad3 = (uint32_t)ids[3] >= ns;
-          const bool any_bad = __any(bad0 || bad1 || bad2 || bad3);
-          if (!(tq0 + 16 <= lim_min && !any_bad)) {
+          if (!(tq0 + 16 <= lim_min && !seg_bad)) {
+            const i32x4 ids = *(const MLA_LDS i32x4*)(idxl + NT * it + 16 * wave + 4 * lg);
+            const uint32_t ns = (uint32_t)p.num_slots;
+            const bool bad0 = (uint32_t)ids[0] >= ns, bad1 = (uint32_t)ids[1] >= ns;
+            const bool bad2 = (uint32_t)ids[2] >= ns, bad3 = (uint32_t)ids[3] >= ns;
 #pragma unroll
             for (int g = 0; g < NRG; ++g)
 #pragma unroll
@@ -920,7 +950,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         // ---- the running maxima (a NaN score leaves them; it poisons the sum)
 #pragma unroll
         for (int g = 0; g < NRG; ++g)
-          rmax[g] = fmaxf(rmax[g], fmaxf(fmaxf(S[g][0], S[g][1]), fmaxf(S[g][2], S[g][3])));
+          rmax[g] = max3f(max3f(rmax[g], S[g][0], S[g][1]), S[g][2], S[g][3]);
         float ps[NRG];
         p_tile<NRG>(S, p.c_log2, nmb, ptb, wave, lane, ps);
         i32x2 v0[8];
