@@ -386,7 +386,8 @@ def main():
         del st
         torch.cuda.empty_cache()
         by_config = {}
-        for name, fq in (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True)):
+        for name, fq in (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True),
+                         ("rank_share", True)):
             if (name, fq) == (args.config, args.fp8_query):
                 continue
             by_config[name + ("_fp8_query" if fq else "")] = config_roofline(torch, evict, name, fq, args.config_iters)

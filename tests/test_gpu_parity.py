@@ -943,7 +943,8 @@ def test_single_split_and_one_token(ops, oracle):
 
 @pytest.mark.parametrize("name,fp8_q", [("batch", None), ("batch_8k", None), ("long", None), ("spec_q4", None),
                                          ("spec_q8", None), ("rank_share", None), ("batch", "codes"),
-                                         ("batch", "quantised"), ("spec_q8", "codes"), ("long", "codes")])
+                                         ("batch", "quantised"), ("spec_q8", "codes"), ("long", "codes"),
+                                         ("rank_share", "codes")])
 def test_full_size_sampled(ops, oracle, name, fp8_q):
     """The bench configuration at full size; the oracle recomputes a few
     sampled requests (their cache rows written by the oracle itself).  With
