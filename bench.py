@@ -23,7 +23,16 @@ median over a short run): the first step of a loop started from an idle
 GPU, and Python's cyclic garbage collector paused the host for up to ~40 ms
 in mid-loop (measured: one pause turned a 200-step warm loop from 82 to 270
 us per step).  So every timed loop starts behind a short spin kernel (about
-0.4 ms) and runs with the collector off (collected once before).
+0.4 ms) and runs with the collector off (collected once before the
+warm-up: a GPU left idle for a few tens of milliseconds runs its next
+launches at lower clocks, so nothing idles it between a warm-up and its
+timed loop).
+
+The partial kernel's own duration (the `roofline` figures) is what its
+dispatch records in the start and stop events it is given
+(mla_time_next_partial), the same span a kernel trace reports; events
+recorded around the call (`us_queued`) also hold the launch's dispatch and
+completion.
 
 Besides the headline workload, the line carries the partial kernel's
 roofline on the other configurations (a short cold partial-only loop each):
@@ -47,6 +56,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP8_MFMA_PEAK_TFLOPS = 5000.0
 LEAD_CYCLES = 1_000_000  # the spin kernel ahead of a timed loop (about 0.4 ms)
+WARM_S = 0.3  # the least warm-up before a timed loop, in seconds of back-to-back launches
 
 
 def parse():
@@ -65,7 +75,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-config-rooflines", action="store_true",
                     help="skip the partial kernel's rooflines on the other configurations")
-    ap.add_argument("--config-iters", type=int, default=20)
+    ap.add_argument("--config-iters", type=int, default=50)
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (the known-size "
@@ -199,6 +209,55 @@ def host_cpu():
     return "%s (%d logical CPUs visible; %d usable by this process)" % (model, n, len(os.sched_getaffinity(0)))
 
 
+def warm_up(torch, launch, n):
+    """n launches, and at least WARM_S seconds of them, ending on a
+    synchronisation; a timed loop follows at once.  A GPU left idle for a
+    few tens of milliseconds (a garbage collection, a workload's synthesis)
+    runs its next launches at lower clocks: after 33 ms idle, 20 cold partial
+    launches on the long workload averaged 330 us against 270 us without the
+    gap, and after 100 ms idle the first 40-60 batch steps took 93-96 us
+    against 89 us."""
+    t_end = time.perf_counter() + WARM_S
+    done = 0
+    while done < n or time.perf_counter() < t_end:
+        for _ in range(10):
+            launch()
+        done += 10
+        torch.cuda.synchronize()
+
+
+def cold_partial_us(torch, evict, st, n):
+    """n cold launches of the partial kernel alone (each after the eviction
+    read), twice.  Returns (kernel, queued): the mean of the durations the
+    kernel records itself (its dispatch takes the start and stop events),
+    and, from a second loop of plain launches, the mean of events recorded
+    on its stream around each call, which also hold the launch's dispatch
+    and completion (about 3 us more on the batch workload)."""
+    import mla_latent_kv_fp8_amd as m
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for e in ev:  # created on first use
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(LEAD_CYCLES)
+    for k0, k1 in ev:
+        evict()
+        m.time_next_partial(k0, k1)
+        st.attend()
+    torch.cuda.synchronize()
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    torch.cuda._sleep(LEAD_CYCLES)
+    for q0, q1 in ev:
+        evict()
+        q0.record()
+        st.attend()
+        q1.record()
+    torch.cuda.synchronize()
+    queued = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    return kern, queued
+
+
 def config_roofline(torch, evict, name, fp8_query, iters):
     """The partial kernel's cold roofline on one more configuration: a short
     partial-only loop, each launch after the eviction read, with its own
@@ -215,24 +274,15 @@ def config_roofline(torch, evict, name, fp8_query, iters):
         st.use_fp8_query(1.0 / 16.0)
         st.quantize_query()
     st.write_new_tokens()
-    for _ in range(3):
-        st.attend()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     gc.collect()
     gc.disable()
-    torch.cuda._sleep(LEAD_CYCLES)
-    for a, b in ev:
-        evict()
-        a.record()
-        st.attend()
-        b.record()
-    torch.cuda.synchronize()
+    warm_up(torch, lambda: (evict(), st.attend()), 3)
+    us, us_queued = cold_partial_us(torch, evict, st, iters)
     gc.enable()
-    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     kv_bytes, flops = algorithmic(w)
     roof, other = roof_of(flops, kv_bytes, us, mixed_peak_tflops() if fp8_query else BF16_MFMA_PEAK_TFLOPS)
-    roof.update({"us": round(us, 2), "other": other, "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
+    roof.update({"us": round(us, 2), "us_queued": round(us_queued, 2), "other": other, "flops_per_launch": flops,
+                 "kv_bytes_per_launch": kv_bytes,
                  "workload": "%s: B=%d qlen=%d heads=%d tokens=%d%s" % (name, w.batch, w.qlen, w.heads,
                                                                         w.total_tokens,
                                                                         ", fp8 query" if fp8_query else "")})
@@ -280,6 +330,10 @@ def cpu_baseline(w, budget_s):
                       (n_req, w.batch, H, done_bytes // 576, t_total)}
 
 
+# the configurations whose partial-kernel rooflines join the bench line
+CONFIG_ROOFLINES = (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True), ("rank_share", True))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -308,12 +362,14 @@ def main():
     evict = Evict(torch)
     torch.cuda.synchronize()
 
+    # collected before the warm-up steps, not between them and the timed
+    # loop: a GPU left idle that long starts the timed steps at lower clocks
+    gc.collect()
+    gc.disable()  # no collector pause inside a timed loop (re-enabled after them)
     for _ in range(args.warmup):
         evict()
         st.run()
     torch.cuda.synchronize()
-    gc.collect()
-    gc.disable()  # no collector pause inside a timed loop (re-enabled after them)
 
     K = args.steps
     # one event pair per step and none inside it: an event recorded between
@@ -353,18 +409,9 @@ def main():
     torch.cuda.synchronize()
     warm_ms = wa.elapsed_time(wb) / K
 
-    # the partial kernel alone (its own events), cold
-    pk = []
-    torch.cuda._sleep(LEAD_CYCLES)
-    for _ in range(K):
-        evict()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        st.attend()
-        b.record()
-        pk.append((a, b))
-    torch.cuda.synchronize()
-    partial_ms = float(np.mean([a.elapsed_time(b) for a, b in pk]))
+    # the partial kernel alone, cold
+    partial_us, partial_us_queued = cold_partial_us(torch, evict, st, K)
+    partial_ms = partial_us * 1e-3
     gc.enable()
 
     kv_bytes, flops = algorithmic(w)
@@ -375,6 +422,7 @@ def main():
     # chip's balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), else HBM
     traffic = None if args.fp8_query else measured_traffic(args.config)
     common = {"traffic": traffic, "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
+              "us_queued": round(partial_us_queued, 2),
               "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
               "flop_per_byte": round(flops / max(kv_bytes, 1), 1)}
     roof, other = roof_of(flops, kv_bytes, partial_ms * 1e3,
@@ -386,8 +434,7 @@ def main():
         del st
         torch.cuda.empty_cache()
         by_config = {}
-        for name, fq in (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True),
-                         ("rank_share", True)):
+        for name, fq in CONFIG_ROOFLINES:
             if (name, fq) == (args.config, args.fp8_query):
                 continue
             by_config[name + ("_fp8_query" if fq else "")] = config_roofline(torch, evict, name, fq, args.config_iters)

@@ -22,12 +22,14 @@
  *   mla_merge_lse       LSE merge of the splits -> latent (bf16)
  *   mla_value_gate      per-head W_UV (bf16 or MXFP4) + FP32 sigmoid gate
  *   mla_merge_value_gate  the merge, W_UV and gate in one call (no latent written)
+ *   mla_time_next_partial  (measurement) events the next partial launch records
  *
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
  *     the argument says "host".  The library keeps no pointer after a call
- *     returns, allocates nothing, and never synchronizes: work is enqueued
- *     on `stream` (a hipStream_t; NULL = the default stream).
+ *     returns (mla_time_next_partial's event handles excepted), allocates
+ *     nothing, and never synchronizes: work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream).
  *   - bf16 data is passed as uint16_t (raw bits), fp8 E4M3 (OCP "fn": bias
  *     7, max 448, 0x7F/0xFF NaN, no infinities) as uint8_t.
  *   - Strides are in ELEMENTS of the pointed-to type; the innermost axis of
@@ -427,6 +429,23 @@ int mla_merge_value_gate(const uint16_t* o_part, int64_t os_split, int64_t os_ro
                          const uint8_t* w_scale, int64_t ws_head, int64_t ws_v, const uint16_t* gate,
                          int64_t g_row, const int32_t* lengths, int32_t rows, int32_t qlen, int32_t heads,
                          uint16_t* out, int64_t out_row, float* lse, int64_t l_row, int64_t l_head, void* stream);
+
+/*
+ * Measurement aid, for a harness that times the partial kernel itself.  The
+ * next launch of the partial kernel by this process (by any of
+ * mla_decode_partial, mla_decode_partial_hostplan, mla_decode_partial_fp8q,
+ * mla_decode_partial_fp8q_hostplan, mla_decode_attend,
+ * mla_decode_attend_noalloc) records start_event when the kernel starts and
+ * stop_event when it ends (hipExtLaunchKernelGGL), so that
+ * hipEventElapsedTime of the two is the kernel's own duration and not that
+ * of the queue around it.  The events are the caller's: hipEvent_t handles
+ * created with timing (the default flags), on the device of that launch,
+ * alive until it has run.  Either may be NULL; NULL, NULL clears a pending
+ * pair.  The library holds the two handles until that one launch takes them
+ * (the only pointers it keeps across calls).  One pending pair per process:
+ * calls from concurrent host threads race for it.  Returns MLA_OK.
+ */
+int mla_time_next_partial(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
         L.mla_merge_value_gate.argtypes = [P, i64, i64, i64, P, i64, i64, i64, i32, i32, P, i64, i64, P, i64,
                                            i64, P, i64, P, i32, i32, i32, P, i64, P, i64, i64, P]
         L.mla_split_plan.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.mla_time_next_partial.argtypes = [P, P]
         L.mla_decode_attend.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32, i32, P, P, i64,
                                         i64, P, i64, i64, P, i64, P]
         L.mla_decode_attend_noalloc.argtypes = [P, i64, i64, i32, i32, i32, P, i64, P, P, f32, f32, i32, i32, i32, P, P,
@@ -70,7 +71,7 @@ def lib() -> ctypes.CDLL:
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
                      "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate",
-                     "mla_decode_attend", "mla_decode_attend_noalloc"):
+                     "mla_decode_attend", "mla_decode_attend_noalloc", "mla_time_next_partial"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -286,6 +287,18 @@ def split_plan(kv_indptr, num_splits: int, num_workers: int, split_min_tokens: i
                               split_min_tokens, bounds.ctypes.data_as(ctypes.c_void_p), ctypes.byref(chunk))
     _check(st, "mla_split_plan")
     return bounds, int(chunk.value)
+
+
+def time_next_partial(start: torch.cuda.Event | None, stop: torch.cuda.Event | None) -> None:
+    """The next partial-kernel launch records `start` and `stop` (timing
+    events, already created: recorded once) at its own start and end, so
+    start.elapsed_time(stop) is the kernel's duration.  None, None clears."""
+    handles = []
+    for e in (start, stop):
+        if e is not None and not e.cuda_event:
+            raise MlaError("time_next_partial: record the event once first (it is created on first use)")
+        handles.append(ctypes.c_void_p(e.cuda_event if e is not None else 0))
+    _check(lib().mla_time_next_partial(*handles), "mla_time_next_partial")
 
 
 def merge_lse(o_part: torch.Tensor, lse_part: torch.Tensor, o: torch.Tensor, lse: torch.Tensor | None = None) -> None:

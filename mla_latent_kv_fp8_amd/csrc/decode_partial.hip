@@ -47,6 +47,8 @@
 //    goes straight to the merged latent; the pieces of a split request go to
 //    workspace slots, and the block that completes a request's count (a
 //    system-scope atomic) merges its splits with the LSE merge's own code.
+#include <hip/hip_ext.h>
+
 #include <mutex>
 #include <type_traits>
 
@@ -1128,10 +1130,26 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   }
 }
 
+// The events that the next launch of the partial kernel records at its own
+// start and end (mla_time_next_partial); taken by that launch.
+static std::mutex g_time_mu;
+static hipEvent_t g_time_ev[2] = {nullptr, nullptr};
+
 template <int NRG, bool QF8, bool PLAN, bool FUSE = false>
 static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, int blocks, hipStream_t s) {
   static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
-  hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, a, pl);
+  hipEvent_t ev[2];
+  {
+    std::lock_guard<std::mutex> lock(g_time_mu);
+    ev[0] = g_time_ev[0];
+    ev[1] = g_time_ev[1];
+    g_time_ev[0] = g_time_ev[1] = nullptr;
+  }
+  if (ev[0] || ev[1])
+    hipExtLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, ev[0], ev[1], 0, a,
+                          pl);
+  else
+    hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, a, pl);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -1487,4 +1505,11 @@ extern "C" int mla_decode_attend_noalloc(const uint16_t* q, int64_t q_stride_row
   return mla::attend_impl(q, q_stride_row, q_stride_head, batch, qlen, heads, kv_cache, num_slots, kv_indptr,
                           kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens, kv_indptr_host,
                           o, o_row, o_head, lse, l_row, l_head, ws, MLA_ATTEND_NOALLOC_MAX_BYTES, stream);
+}
+
+extern "C" int mla_time_next_partial(void* start_event, void* stop_event) {
+  std::lock_guard<std::mutex> lock(mla::g_time_mu);
+  mla::g_time_ev[0] = (hipEvent_t)start_event;
+  mla::g_time_ev[1] = (hipEvent_t)stop_event;
+  return MLA_OK;
 }

@@ -469,6 +469,48 @@ def test_hostplan_fp8_query_is_the_in_kernel_partition_bit_for_bit(ops, name, ba
     assert np.array_equal(got[0][0], got[1][0]), "o_part differs"
 
 
+@pytest.mark.parametrize("host_plan", [False, True])
+def test_timed_launch_is_the_untimed_launch(ops, host_plan):
+    """mla_time_next_partial: the launch that takes the events writes the
+    same o_part and lse_part bytes as an untimed one, its recorded duration
+    is positive and within the events recorded around the call, and the pair
+    is taken by that one launch (the next launch records nothing)."""
+    import mla_latent_kv_fp8_amd as m
+    from mla_latent_kv_fp8_amd import synth
+    from mla_latent_kv_fp8_amd.step import DeviceStep
+
+    _announce(f"timed partial launch, host plan={host_plan}")
+    w = synth.make("batch", batch=6, len_range=(100, 900))
+    st = DeviceStep(w, num_workers=8)
+    st.host_plan = host_plan
+    st.write_new_tokens()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    got = []
+    for timed in (False, True):
+        st.o_part.fill_(0)
+        st.lse_part.fill_(0)
+        if timed:
+            ev[2].record()
+            m.time_next_partial(ev[0], ev[1])
+        st.attend()
+        if timed:
+            ev[3].record()
+        torch.cuda.synchronize()
+        got.append((_np_bf16(st.o_part), st.lse_part.cpu().numpy().view(np.uint32)))
+    assert np.array_equal(got[0][1], got[1][1]), "lse_part differs"
+    assert np.array_equal(got[0][0], got[1][0]), "o_part differs"
+    kern, outer = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < kern <= outer, (kern, outer)
+    # taken: a second launch leaves the events where the first put them
+    st.attend()
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == kern
+    m.time_next_partial(None, None)
+
+
 def test_requests_shorter_than_the_window(ops, oracle):
     """qlen 4 with requests of 1, 2, 3, 0 and 6 tokens: row j of a window
     sees max(0, L - qlen + j + 1) tokens, so the first rows of the short
