@@ -584,20 +584,13 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   MLA_LDS uint8_t* qarea = (MLA_LDS uint8_t*)qarea_;
   const VOffsets vo = v_offsets(wave, lane);
 
-  // ---- block -> (worker, row block); the row blocks of a worker share an
-  // XCD (and its L2), workers interleave across the 8 XCDs
-  int u, rb;
-  {
-    const int bid = blockIdx.x;
-    if (p.num_workers % 8 == 0) {
-      const int slot = bid >> 3;
-      u = (bid & 7) + 8 * (slot / p.n_rb);
-      rb = slot % p.n_rb;
-    } else {
-      u = bid / p.n_rb;
-      rb = bid % p.n_rb;
-    }
-  }
+  // ---- block -> (worker, row block), from the grid alone, so that no
+  // argument read waits for another: the grid is (g, row blocks, workers /
+  // g), g = 8 when num_workers is a multiple of 8, else 1.  Workgroups go to
+  // the 8 XCDs round robin in linear order (x first), so with g = 8 the row
+  // blocks of a worker (linear ids 8 apart) share an XCD and its L2, start
+  // together, and workers interleave across the XCDs.
+  const int u = blockIdx.x + gridDim.x * blockIdx.z, rb = blockIdx.y;
 
   // ---- the split partition: T, L_max -> chunk, and the requests this
   // unit covers
@@ -1136,8 +1129,10 @@ static std::mutex g_time_mu;
 static hipEvent_t g_time_ev[2] = {nullptr, nullptr};
 
 template <int NRG, bool QF8, bool PLAN, bool FUSE = false>
-static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, int blocks, hipStream_t s) {
+static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, hipStream_t s) {
   static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
+  const unsigned g = a.num_workers % 8 == 0 ? 8 : 1;
+  const dim3 grid(g, (unsigned)a.n_rb, (unsigned)a.num_workers / g);
   hipEvent_t ev[2];
   {
     std::lock_guard<std::mutex> lock(g_time_mu);
@@ -1146,10 +1141,9 @@ static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, int blocks, hi
     g_time_ev[0] = g_time_ev[1] = nullptr;
   }
   if (ev[0] || ev[1])
-    hipExtLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, ev[0], ev[1], 0, a,
-                          pl);
+    hipExtLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), grid, dim3(256), 0, s, ev[0], ev[1], 0, a, pl);
   else
-    hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), dim3(blocks), dim3(256), 0, s, a, pl);
+    hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), grid, dim3(256), 0, s, a, pl);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -1233,7 +1227,7 @@ namespace mla {
 // Argument checks and kernel arguments shared by the partial and the fused
 // entry points (bf16 or fp8 query).  q_scale multiplies every score (1 for
 // bf16).  Sets the row-block geometry.
-static int common_args(PartialArgs& a, int& nrg, int& blocks, const void* q, bool q_fp8, int64_t q_stride_row,
+static int common_args(PartialArgs& a, int& nrg, const void* q, bool q_fp8, int64_t q_stride_row,
                        int64_t q_stride_head, float q_scale, int32_t batch, int32_t qlen, int32_t heads,
                        const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
                        const int32_t* kv_indices, float sm_scale, float kv_scale, int32_t num_splits,
@@ -1252,9 +1246,8 @@ static int common_args(PartialArgs& a, int& nrg, int& blocks, const void* q, boo
   // rows per block: 16, 32 or 48 (larger requests take several blocks)
   nrg = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
   const int n_rb = (int)((M + 16 * nrg - 1) / (16 * nrg));
-  const int64_t nb = (int64_t)num_workers * n_rb;
-  if (nb > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
-  blocks = (int)nb;
+  // the grid is (g, n_rb, num_workers / g), g = 8 or 1 (n_rb <= 21846 here)
+  if (num_workers / (num_workers % 8 == 0 ? 8 : 1) > 65535) return MLA_ERR_UNSUPPORTED;
   a = PartialArgs{};
   a.q = q_fp8 ? nullptr : (const uint16_t*)q;
   a.q8 = q_fp8 ? (const uint8_t*)q : nullptr;
@@ -1280,8 +1273,8 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (batch == 0) return MLA_OK;
   if (!o_part || !lse_part) return MLA_ERR_INVALID;
   PartialArgs a;
-  int nrg = 3, blocks = 0;
-  int st = common_args(a, nrg, blocks, q, q_fp8, q_stride_row, q_stride_head, q_scale, batch, qlen, heads, kv_cache,
+  int nrg = 3;
+  int st = common_args(a, nrg, q, q_fp8, q_stride_row, q_stride_head, q_scale, batch, qlen, heads, kv_cache,
                        num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens);
   if (st != MLA_OK) return st;
   // 8-byte partial stores
@@ -1300,29 +1293,29 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (st == MLA_OK) {
     if (q_fp8) {
       switch (nrg) {
-        case 1: return launch<1, true, true>(a, pl, blocks, s);
-        case 2: return launch<2, true, true>(a, pl, blocks, s);
-        default: return launch<3, true, true>(a, pl, blocks, s);
+        case 1: return launch<1, true, true>(a, pl, s);
+        case 2: return launch<2, true, true>(a, pl, s);
+        default: return launch<3, true, true>(a, pl, s);
       }
     }
     switch (nrg) {
-      case 1: return launch<1, false, true>(a, pl, blocks, s);
-      case 2: return launch<2, false, true>(a, pl, blocks, s);
-      default: return launch<3, false, true>(a, pl, blocks, s);
+      case 1: return launch<1, false, true>(a, pl, s);
+      case 2: return launch<2, false, true>(a, pl, s);
+      default: return launch<3, false, true>(a, pl, s);
     }
   }
   const UnitPlan<false> none;
   if (q_fp8) {
     switch (nrg) {
-      case 1: return launch<1, true, false>(a, none, blocks, s);
-      case 2: return launch<2, true, false>(a, none, blocks, s);
-      default: return launch<3, true, false>(a, none, blocks, s);
+      case 1: return launch<1, true, false>(a, none, s);
+      case 2: return launch<2, true, false>(a, none, s);
+      default: return launch<3, true, false>(a, none, s);
     }
   }
   switch (nrg) {
-    case 1: return launch<1, false, false>(a, none, blocks, s);
-    case 2: return launch<2, false, false>(a, none, blocks, s);
-    default: return launch<3, false, false>(a, none, blocks, s);
+    case 1: return launch<1, false, false>(a, none, s);
+    case 2: return launch<2, false, false>(a, none, s);
+    default: return launch<3, false, false>(a, none, s);
   }
 }
 
@@ -1357,8 +1350,8 @@ static int attend_impl(const uint16_t* q, int64_t q_stride_row, int64_t q_stride
   if (batch == 0) return MLA_OK;
   if (!o || !workspace || !indptr_host) return MLA_ERR_INVALID;
   PartialArgs a;
-  int nrg = 3, blocks = 0;
-  int st = common_args(a, nrg, blocks, q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
+  int nrg = 3;
+  int st = common_args(a, nrg, q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
                        num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits, num_workers, split_min_tokens);
   if (st != MLA_OK) return st;
   if (num_workers > PLAN_UNITS) return MLA_ERR_UNSUPPORTED;
@@ -1382,9 +1375,9 @@ static int attend_impl(const uint16_t* q, int64_t q_stride_row, int64_t q_stride
   a.ws_o_off = (int32_t)(lay.cnt_bytes + lay.lse_bytes);
   hipStream_t s = (hipStream_t)stream;
   switch (nrg) {
-    case 1: return launch<1, false, true, true>(a, pl, blocks, s);
-    case 2: return launch<2, false, true, true>(a, pl, blocks, s);
-    default: return launch<3, false, true, true>(a, pl, blocks, s);
+    case 1: return launch<1, false, true, true>(a, pl, s);
+    case 2: return launch<2, false, true, true>(a, pl, s);
+    default: return launch<3, false, true, true>(a, pl, s);
   }
 }
 
