@@ -7,6 +7,10 @@
 namespace mla {
 
 // One thread per 8 consecutive columns of one token: 72 threads per row.
+// The row's 8 values are loaded together with the token's slot (one memory
+// round trip, not two: a row is read even when its slot is skipped); VEC:
+// one 16-byte load (both sources 16-byte aligned, strides multiples of 8).
+template <bool VEC>
 __global__ void __launch_bounds__(256) kv_write_kernel(const uint16_t* __restrict__ kv_c,
                                                        int64_t kv_c_stride,
                                                        const uint16_t* __restrict__ k_pe,
@@ -18,14 +22,23 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const uint16_t* __restric
   if (item >= (int64_t)n * 72) return;
   int64_t i = item / 72;
   int c0 = (int)(item % 72) * 8;
-  int64_t slot = slots[i];
-  if (slot < 0 || slot >= num_slots) return;
   const uint16_t* src = c0 < MLA_D_LATENT ? kv_c + i * kv_c_stride + c0
                                           : k_pe + i * k_pe_stride + (c0 - MLA_D_LATENT);
+  uint32_t w[4];
+  if constexpr (VEC) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = raw[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = (uint32_t)src[2 * k] | ((uint32_t)src[2 * k + 1] << 16);
+  }
+  const int64_t slot = slots[i];
+  if (slot < 0 || slot >= num_slots) return;
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float x = bf16_bits_to_f32(src[e]);
+    float x = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     uint32_t b = f32_to_fp8_e4m3(x / kv_scale);  // correctly rounded binary32 division
     if (e < 4)
       lo |= b << (8 * e);
@@ -87,9 +100,13 @@ extern "C" int mla_kv_write(const uint16_t* kv_c, int64_t kv_c_stride, const uin
   int64_t items = (int64_t)n * 72;
   int64_t blocks = (items + 255) / 256;
   if (blocks > 0x7FFFFFFF) return MLA_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(mla::kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
-                     kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, n, kv_cache, num_slots,
-                     kv_scale);
+  const bool vec = ((((uintptr_t)kv_c) | ((uintptr_t)k_pe)) % 16 == 0) && ((kv_c_stride | k_pe_stride) % 8 == 0);
+  if (vec)
+    hipLaunchKernelGGL(mla::kv_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, n, kv_cache, num_slots, kv_scale);
+  else
+    hipLaunchKernelGGL(mla::kv_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                       kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, n, kv_cache, num_slots, kv_scale);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

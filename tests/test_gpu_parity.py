@@ -56,8 +56,12 @@ def _announce(msg):
 
 # ------------------------------------------------------------------ kv_write
 
-def test_kv_write_bitexact_edge_values(ops, oracle):
-    _announce("kv_write edge values")
+@pytest.mark.parametrize("aligned", [True, False])
+def test_kv_write_bitexact_edge_values(ops, oracle, aligned):
+    """Strided views of a fused projection: 16-byte aligned sources with
+    strides of a multiple of 8 (the 16-byte load path) and odd ones (the
+    2-byte load path)."""
+    _announce(f"kv_write edge values, aligned={aligned}")
     rng = np.random.default_rng(100)
     n, slots = 300, 401
     x = (rng.standard_normal((n, 576)) * 40).astype(np.float32)
@@ -71,17 +75,18 @@ def test_kv_write_bitexact_edge_values(ops, oracle):
     x[2, 8:12] = [np.nan, -0.0, 1e-30, -1e-6]
     from mla_latent_kv_fp8_amd.synth import to_bf16_bits
     bits = to_bf16_bits(x)
-    fused = np.zeros((n, 2112), dtype=np.uint16)  # strided views of a fused projection
-    fused[:, 1536:2048] = bits[:, :512]
-    fused[:, 2048:2112] = bits[:, 512:]
+    o = 1536 if aligned else 1537
+    fused = np.zeros((n, 2112 if aligned else 2115), dtype=np.uint16)  # strided views of a fused projection
+    fused[:, o:o + 512] = bits[:, :512]
+    fused[:, o + 512:o + 576] = bits[:, 512:]
     slot_map = rng.permutation(slots)[:n].astype(np.int64)
     slot_map[5] = -1
     for kv_scale in (1.0, 0.05, 3.0):
         cache = torch.full((slots, 576), 0x7F, dtype=torch.uint8, device="cuda")
         f = _bf16_dev(fused)
-        ops.kv_write(f[:, 1536:2048], f[:, 2048:], torch.from_numpy(slot_map).cuda(), cache, kv_scale)
+        ops.kv_write(f[:, o:o + 512], f[:, o + 512:o + 576], torch.from_numpy(slot_map).cuda(), cache, kv_scale)
         torch.cuda.synchronize()
-        want = oracle.kv_write(fused[:, 1536:2048], fused[:, 2048:], slot_map,
+        want = oracle.kv_write(fused[:, o:o + 512], fused[:, o + 512:o + 576], slot_map,
                                np.full((slots, 576), 0x7F, np.uint8), kv_scale)
         assert np.array_equal(cache.cpu().numpy(), want), kv_scale
 
