@@ -36,9 +36,10 @@ completion.
 
 Besides the headline workload, the line carries the partial kernel's
 roofline on the other configurations (a short cold partial-only loop each):
-rank_share against HBM, spec_q8 and long against bf16 MFMA, and the batch
-workload's fp8-query call against the MFMA peak of its mix (QK on the fp8
-MFMA, PV on the bf16 MFMA).  Prints ONE JSON line.
+batch_8k (64 requests of exactly 8192 tokens), spec_q4, spec_q8 and long
+against bf16 MFMA, rank_share against HBM, and the fp8-query call on the
+batch workload and on the rank share against the peaks of its mix (QK on
+the fp8 MFMA, PV on the bf16 MFMA).  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -331,7 +332,8 @@ def cpu_baseline(w, budget_s):
 
 
 # the configurations whose partial-kernel rooflines join the bench line
-CONFIG_ROOFLINES = (("rank_share", False), ("spec_q8", False), ("long", False), ("batch", True), ("rank_share", True))
+CONFIG_ROOFLINES = (("batch_8k", False), ("rank_share", False), ("spec_q4", False), ("spec_q8", False), ("long", False),
+                    ("batch", True), ("rank_share", True))
 
 
 def main():
