@@ -2,7 +2,11 @@
 
 A step is the whole hot path over one batch of synthetic input already
 resident in HBM: kv_write (the step's new tokens) -> decode_partial ->
-merge_lse -> value_gate.  Default workload: the batch-decode configuration
+merge_lse -> value_gate, where the cache write runs inside the partials'
+launch (mla_kv_write_decode_partial_hostplan) when each request has one new
+token (--write auto; measured faster there, and slower with 4 or 8 new
+tokens per request, whose encodes every row block's workgroup repeats).
+Default workload: the batch-decode configuration
 (64 requests, qlen 1, 96 heads in a 128-head query buffer, fp8 KV with
 kv_scale 0.05, context lengths uniform in [1024, 8192], 4 empty requests,
 bf16 W_UV).
@@ -28,7 +32,8 @@ warm-up: a GPU left idle for a few tens of milliseconds runs its next
 launches at lower clocks, so nothing idles it between a warm-up and its
 timed loop).
 
-The partial kernel's own duration (the `roofline` figures) is what its
+The partial kernel's own duration (the `roofline` figures; with the cache
+write in it when the step fuses it) is what its
 dispatch records in the start and stop events it is given
 (mla_time_next_partial), the same span a kernel trace reports; events
 recorded around the call (`us_queued`) also hold the launch's dispatch and
@@ -73,6 +78,10 @@ def parse():
     ap.add_argument("--post", choices=("fused", "separate"), default="separate",
                     help="merge + W_UV + gate as mla_merge_lse then mla_value_gate (the faster, measured), "
                          "or as one call (mla_merge_value_gate; needs value heads == attention heads)")
+    ap.add_argument("--write", choices=("auto", "fused", "separate"), default="auto",
+                    help="the new tokens' cache write inside the partials' launch "
+                         "(mla_kv_write_decode_partial_hostplan) or as mla_kv_write before it; auto: fused "
+                         "for one new token per request (measured faster there), separate for more")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-config-rooflines", action="store_true",
                     help="skip the partial kernel's rooflines on the other configurations")
@@ -141,6 +150,12 @@ def roof_of(flops, kv_bytes, us, mfma_peak):
     return hbm, mfma
 
 
+def step_bytes_kv_write(w):
+    """The cache write's algorithmic bytes: each new token's bf16 row and
+    slot read, its fp8 row written."""
+    return int((w.slot_mapping >= 0).sum()) * (2 * 576 + 8 + 576)
+
+
 def step_bytes(w, num_workers, split_min):
     """Algorithmic bytes of one whole step, by tensor: each byte a kernel must
     read or write once.  Live partial entries (splits that hold tokens for a
@@ -156,10 +171,9 @@ def step_bytes(w, num_workers, split_min):
             vis = max(0, L - w.qlen + j + 1)
             b = np.minimum(bounds[r], vis)
             live += int((np.diff(b) > 0).sum())
-    n_new = int((w.slot_mapping >= 0).sum())
     w_bytes = VH * 128 * 512 * 2 if w.w_format == "bf16" else VH * 128 * (256 + 16)
     parts = {
-        "kv_write": n_new * (2 * 576 + 8 + 576),
+        "kv_write": step_bytes_kv_write(w),
         "query": S * H * 576 * 2,
         "kv_cache": int(w.total_tokens) * (576 + 4),
         "partials": 2 * live * H * (512 * 2 + 4),  # written by the partial kernel, read by the merge
@@ -171,14 +185,16 @@ def step_bytes(w, num_workers, split_min):
     return parts
 
 
-def measured_traffic(config):
-    """HBM bytes per launch of the partial kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-probe calibration),
-    or None when that summary was taken on other kernel source."""
+def measured_traffic(config, fused_write=False):
+    """HBM bytes per launch of the partial kernel (with the cache write in
+    it: fused_write) from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, scaled by the copy-probe calibration), or None when that
+    summary was taken on other kernel source."""
     import hashlib
 
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", "partial_kernel_%s_hbm_traffic.md" % config)
+    path = os.path.join(here, "profiles", "partial_kernel_%s%s_hbm_traffic.md"
+                        % ("kv_write_fused_" if fused_write else "", config))
     if not os.path.exists(path):
         return None
     fields = {}
@@ -228,8 +244,8 @@ def warm_up(torch, launch, n):
 
 
 def cold_partial_us(torch, evict, st, n):
-    """n cold launches of the partial kernel alone (each after the eviction
-    read), twice.  Returns (kernel, queued): the mean of the durations the
+    """n cold launches of the step's partial kernel alone (st.partials(),
+    each after the eviction read), twice.  Returns (kernel, queued): the mean of the durations the
     kernel records itself (its dispatch takes the start and stop events),
     and, from a second loop of plain launches, the mean of events recorded
     on its stream around each call, which also hold the launch's dispatch
@@ -245,14 +261,14 @@ def cold_partial_us(torch, evict, st, n):
     for k0, k1 in ev:
         evict()
         m.time_next_partial(k0, k1)
-        st.attend()
+        st.partials()
     torch.cuda.synchronize()
     kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     torch.cuda._sleep(LEAD_CYCLES)
     for q0, q1 in ev:
         evict()
         q0.record()
-        st.attend()
+        st.partials()
         q1.record()
     torch.cuda.synchronize()
     queued = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
@@ -361,6 +377,7 @@ def main():
         # 1/16 for the N(0,1) synthetic query), then attends on the fp8 codes
         st.use_fp8_query(1.0 / 16.0)
     st.fused_post = fused_post = args.post == "fused" and w.value_heads == w.heads
+    st.fused_write = fused_write = args.write == "fused" or (args.write == "auto" and w.qlen == 1)
     evict = Evict(torch)
     torch.cuda.synchronize()
 
@@ -394,10 +411,11 @@ def main():
     for i in range(K):
         evict()
         ea[i][0].record()
-        st.write_new_tokens()
+        if not fused_write:
+            st.write_new_tokens()
         if st.q_bf16 is not None:
             st.quantize_query()
-        st.attend()
+        st.partials()
         ea[i][1].record()
     torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in ea]
@@ -419,15 +437,22 @@ def main():
     kv_bytes, flops = algorithmic(w)
     ms = float(np.mean(step_ms))
     value = kv_bytes / (ms * 1e-3) / 1e9
+    # the fused launch also reads the new rows and slots and writes their
+    # cache rows
+    write_bytes = step_bytes_kv_write(w) if fused_write else 0
     sb = step_bytes(w, st.num_workers, st.split_min)
     # the partial kernel's bound: MFMA when its flops per KV byte exceed the
     # chip's balance (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), else HBM
-    traffic = None if args.fp8_query else measured_traffic(args.config)
-    common = {"traffic": traffic, "kernel": "partial_kernel (decode_partial)", "us": round(partial_ms * 1e3, 2),
-              "us_queued": round(partial_us_queued, 2),
-              "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes,
-              "flop_per_byte": round(flops / max(kv_bytes, 1), 1)}
-    roof, other = roof_of(flops, kv_bytes, partial_ms * 1e3,
+    traffic = None if args.fp8_query else measured_traffic(args.config, fused_write)
+    common = {"traffic": traffic,
+              "kernel": ("partial_kernel (kv_write fused into decode_partial)" if fused_write
+                         else "partial_kernel (decode_partial)"),
+              "us": round(partial_ms * 1e3, 2), "us_queued": round(partial_us_queued, 2),
+              "flops_per_launch": flops, "kv_bytes_per_launch": kv_bytes + write_bytes,
+              "flop_per_byte": round(flops / max(kv_bytes + write_bytes, 1), 1)}
+    if fused_write:
+        common["kv_write_bytes_per_launch"] = write_bytes
+    roof, other = roof_of(flops, kv_bytes + write_bytes, partial_ms * 1e3,
                           mixed_peak_tflops() if args.fp8_query else BF16_MFMA_PEAK_TFLOPS)
     roof = dict(roof, **common)
     other_key = "roofline_hbm" if roof["bound"] == "mfma" else "roofline_mfma"
@@ -466,6 +491,8 @@ def main():
                                                                   else " bf16", w.total_tokens, w.kv_scale,
                                                                   w.num_splits, w.num_workers, w.w_format),
                    "post": "merge+W_UV+gate fused" if fused_post else "merge, then W_UV+gate",
+                   "cache_write": ("fused into the partials' launch" if fused_write
+                                   else "mla_kv_write before the partials"),
                    "global_batch": w.batch, "seq_len": int(w.lengths.max())},
         "roofline": roof,
         # the other roof of the same kernel, for reference

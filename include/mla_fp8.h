@@ -16,6 +16,8 @@
  *   mla_decode_partial_fp8q  the same for an fp8 query with a per-tensor scale
  *   mla_decode_partial_hostplan, mla_decode_partial_fp8q_hostplan  the two
  *                       above with the split partition computed on the host
+ *   mla_kv_write_decode_partial_hostplan, _fp8q_hostplan  the cache write
+ *                       and the host-planned partials in one launch
  *   mla_decode_attend   the attention and the LSE merge in one launch ->
  *                       latent (bf16) and LSE, with a caller's workspace
  *   mla_decode_attend_noalloc  the same with the library's own workspace
@@ -272,6 +274,62 @@ int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_stride_row, in
                                      uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                                      float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
                                      const int32_t* kv_indptr_host, void* stream);
+
+/*
+ * The cache write of the new tokens ([MLA] `pre`: do_kv_cache_update) and
+ * the split-KV partials over the updated cache ([MLA] `attend`) in one
+ * launch: the cache bytes of mla_kv_write followed by the partials of
+ * mla_decode_partial_hostplan, bit for bit.  Arguments: those of
+ * mla_kv_write for the new tokens (without n, num_slots and kv_scale, which
+ * are the partials' own), new_per_request, then those of
+ * mla_decode_partial_hostplan, with kv_cache written.
+ *   new_per_request  k, 1..8: the batch * k new tokens are the last k
+ *                tokens of each request, request-major: kv_c, k_pe and
+ *                slot_mapping row r * k + j is request r's token at
+ *                position L_r - k + j (kv_indices[kv_indptr[r] + L_r - k + j]
+ *                normally names slot_mapping[r * k + j]).  A token at a
+ *                negative position (L_r < k) is written and not attended.
+ *   kv_c, k_pe   16-byte aligned, strides multiples of 8 elements.
+ * Each workgroup that attends a new token writes that token's row itself
+ * before it loads any cache row of its piece, so the launch needs no
+ * ordering between workgroups.  In return, a slot this call writes must be
+ * named in kv_indices at no position other than its own token's (as a slot
+ * freshly given to a request is); where it is, which row such a read sees
+ * is unspecified.  Slots must be distinct, as for mla_kv_write; a slot
+ * outside [0, num_slots) skips its token.
+ * Errors: those of mla_decode_partial_hostplan, and MLA_ERR_INVALID for a
+ * null kv_c, k_pe or slot_mapping, kv_c_stride < 512, k_pe_stride < 64 or
+ * new_per_request outside 1..8; MLA_ERR_UNSUPPORTED for rows that are not
+ * 16-byte aligned.  batch = 0 is a no-op.
+ */
+int mla_kv_write_decode_partial_hostplan(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                                         int64_t k_pe_stride, const int64_t* slot_mapping,
+                                         int32_t new_per_request, const uint16_t* q, int64_t q_stride_row,
+                                         int64_t q_stride_head, int32_t batch, int32_t qlen, int32_t heads,
+                                         uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
+                                         const int32_t* kv_indices, float sm_scale, float kv_scale,
+                                         int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
+                                         uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
+                                         float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+                                         const int32_t* kv_indptr_host, void* stream);
+
+/*
+ * mla_kv_write_decode_partial_hostplan for an fp8 query: the new tokens'
+ * arguments as there, then those of mla_decode_partial_fp8q_hostplan (with
+ * kv_cache written); the partials are those of
+ * mla_decode_partial_fp8q_hostplan after mla_kv_write, bit for bit.
+ */
+int mla_kv_write_decode_partial_fp8q_hostplan(const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe,
+                                              int64_t k_pe_stride, const int64_t* slot_mapping,
+                                              int32_t new_per_request, const uint8_t* q8, int64_t q_stride_row,
+                                              int64_t q_stride_head, float q_scale, int32_t batch, int32_t qlen,
+                                              int32_t heads, uint8_t* kv_cache, int64_t num_slots,
+                                              const int32_t* kv_indptr, const int32_t* kv_indices,
+                                              float sm_scale, float kv_scale, int32_t num_splits,
+                                              int32_t num_workers, int32_t split_min_tokens, uint16_t* o_part,
+                                              int64_t os_split, int64_t os_row, int64_t os_head,
+                                              float* lse_part, int64_t ls_split, int64_t ls_row,
+                                              int64_t ls_head, const int32_t* kv_indptr_host, void* stream);
 
 /*
  * The attention and its LSE merge in one launch ([MLA] `m1c_inputs`: the

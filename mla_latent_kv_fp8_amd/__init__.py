@@ -50,6 +50,10 @@ def lib() -> ctypes.CDLL:
         L.mla_decode_partial_fp8q_hostplan.argtypes = [P, i64, i64, f32, i32, i32, i32, P, i64, P, P, f32,
                                                        f32, i32, i32, i32, P, i64, i64, i64, P, i64, i64,
                                                        i64, P, P]
+        L.mla_kv_write_decode_partial_hostplan.argtypes = [P, i64, P, i64, P, i32] + \
+            L.mla_decode_partial_hostplan.argtypes
+        L.mla_kv_write_decode_partial_fp8q_hostplan.argtypes = [P, i64, P, i64, P, i32] + \
+            L.mla_decode_partial_fp8q_hostplan.argtypes
         L.mla_concat_quant_fp8.argtypes = [P, i64, i64, P, i64, i64, f32, i32, i32, P, i64, i64, P]
         L.mla_absorb_query.argtypes = [P, i64, i64, P, i64, i64, P, i64, i64, P, i64, i64, i32, i32, i32, f32, P,
                                        i64, i64, P]
@@ -71,7 +75,8 @@ def lib() -> ctypes.CDLL:
                                      P, i64, P]
         for name in ("mla_kv_write", "mla_absorb_query", "mla_concat_quant_fp8", "mla_decode_partial", "mla_decode_partial_fp8q",
                      "mla_decode_partial_hostplan", "mla_decode_partial_fp8q_hostplan", "mla_split_plan", "mla_merge_lse", "mla_value_gate", "mla_merge_value_gate",
-                     "mla_decode_attend", "mla_decode_attend_noalloc", "mla_time_next_partial"):
+                     "mla_decode_attend", "mla_decode_attend_noalloc", "mla_time_next_partial",
+                     "mla_kv_write_decode_partial_hostplan", "mla_kv_write_decode_partial_fp8q_hostplan"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -211,6 +216,57 @@ def decode_partial_hostplan(q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: 
     decode_partial with the split partition computed on the host from
     kv_indptr_host."""
     decode_partial(q, kv_cache, kv_indptr, kv_indices, o_part, lse_part, kv_indptr_host=kv_indptr_host, **kw)
+
+
+def kv_write_decode_partial_hostplan(kv_c: torch.Tensor, k_pe: torch.Tensor, slot_mapping: torch.Tensor,
+                                     q: torch.Tensor, kv_cache: torch.Tensor, kv_indptr: torch.Tensor,
+                                     kv_indices: torch.Tensor, o_part: torch.Tensor, lse_part: torch.Tensor,
+                                     kv_indptr_host: np.ndarray, *, qlen: int, heads: int, sm_scale: float,
+                                     kv_scale: float, num_workers: int = 256, split_min_tokens: int = 256,
+                                     q_scale: float | None = None) -> None:
+    """mla_kv_write_decode_partial_hostplan / _fp8q_hostplan: kv_write of
+    the batch * k new tokens (the last k of each request, request-major:
+    kv_c, k_pe [batch*k, .] bf16, slot_mapping [batch*k] int64) and
+    decode_partial_hostplan over the updated cache, in one launch."""
+    batch = kv_indptr.shape[0] - 1
+    n = slot_mapping.shape[0]
+    if batch < 1 or n % batch != 0:
+        raise MlaError("slot_mapping must hold the same number of new tokens for each request")
+    k = n // batch
+    if kv_c.shape[0] != n or k_pe.shape[0] != n:
+        raise MlaError("kv_c and k_pe must hold one row per new token")
+    if kv_c.shape[-1] < D_LATENT or k_pe.shape[-1] < D_ROPE:
+        raise MlaError("kv_c rows hold 512 values, k_pe rows 64")
+    S = q.shape[0]
+    if S != batch * qlen:
+        raise MlaError("q has %d rows, expected batch*qlen = %d" % (S, batch * qlen))
+    ns = o_part.shape[0]
+    if lse_part.shape[0] != ns or o_part.shape[1] < S or o_part.shape[2] < heads or o_part.shape[3] != D_LATENT:
+        raise MlaError("bad partial buffer shapes")
+    if q.shape[-1] != D_QK or q.shape[1] < heads:
+        raise MlaError("q must be [S, >=heads, 576]")
+    fp8_q = q.dtype in _U8
+    if fp8_q != (q_scale is not None):
+        raise MlaError("an fp8 query takes q_scale, a bf16 query does not")
+    ih = np.ascontiguousarray(kv_indptr_host, dtype=np.int32)
+    if ih.shape != (batch + 1,):
+        raise MlaError("kv_indptr_host must hold batch+1 offsets")
+    new = (_dev(kv_c, "kv_c", _BF16), kv_c.stride(0), _dev(k_pe, "k_pe", _BF16), k_pe.stride(0),
+           _dev(slot_mapping, "slot_mapping", (torch.int64,)), k)
+    rest = (batch, qlen, heads, _dev(kv_cache, "kv_cache", _U8), kv_cache.shape[0],
+            _dev(kv_indptr, "kv_indptr", (torch.int32,)), _dev(kv_indices, "kv_indices", (torch.int32,)),
+            float(sm_scale), float(kv_scale), ns, int(num_workers), int(split_min_tokens),
+            _dev(o_part, "o_part", _BF16), o_part.stride(0), o_part.stride(1), o_part.stride(2),
+            _dev(lse_part, "lse_part", (torch.float32,)), lse_part.stride(0), lse_part.stride(1),
+            lse_part.stride(2), ih.ctypes.data_as(ctypes.c_void_p), _stream())
+    if fp8_q:
+        st = lib().mla_kv_write_decode_partial_fp8q_hostplan(*new, _dev(q, "q", _U8), q.stride(0), q.stride(1),
+                                                             float(q_scale), *rest)
+        _check(st, "mla_kv_write_decode_partial_fp8q_hostplan")
+    else:
+        st = lib().mla_kv_write_decode_partial_hostplan(*new, _dev(q, "q", _BF16), q.stride(0), q.stride(1),
+                                                        *rest)
+        _check(st, "mla_kv_write_decode_partial_hostplan")
 
 
 def decode_attend_workspace_bytes(batch: int, qlen: int, heads: int, num_workers: int) -> int:

@@ -94,6 +94,69 @@ __device__ __forceinline__ uint32_t f32_to_fp8_e4m3(float v) {
   return code | sign;
 }
 
+// 8 bf16 (dword k holds elements 2k, 2k+1 in its low, high half) -> the
+// 8 fp8 E4M3 codes of x / scale (correctly rounded divisions), element 0
+// in the low byte of the first dword.
+__device__ __forceinline__ u32x2 encode_fp8x8(const uint32_t w[4], float scale) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t b = f32_to_fp8_e4m3(bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) / scale);
+    if (e < 4)
+      lo |= b << (8 * e);
+    else
+      hi |= b << (8 * (e - 4));
+  }
+  return u32x2{lo, hi};
+}
+
+// 4 bf16 (w0: elements 0, 1; w1: elements 2, 3; low half first) -> the 4
+// fp8 E4M3 codes encode_fp8x8 gives for them (of x / scale, the division
+// correctly rounded), element 0 in the low byte; rscale = 1 / scale rounded
+// to nearest.  With rscale normal and finite, q = |x| * rscale carries two
+// roundings of relative size 2^-24 at most, so the correctly rounded
+// quotient lies within 8 binary32 steps of q (6 at most, where q and the
+// quotient fall in neighbouring binades), and the encoder is monotone in
+// the magnitude: where the
+// magnitudes 8 steps below and above q get the same code, that code is the
+// quotient's.  The codes come from v_cvt_pk_fp8_f32 on magnitudes held to
+// [0, 448] (where it rounds as f32_to_fp8_e4m3 does, to nearest even, for
+// every binary32 input).  Near a boundary of the fp8 grid (about one value
+// in 10^5), for a NaN, and for every value when rscale is subnormal or
+// infinite (scale above 2^126 or below 2^-126), the division and
+// f32_to_fp8_e4m3 decide.
+__device__ __forceinline__ uint32_t encode_fp8x4_fast(uint32_t w0, uint32_t w1, float scale, float rscale) {
+  constexpr uint32_t kMax = 0x43E00000u;  // 448
+  const uint32_t e[4] = {w0 & 0xFFFFu, w0 >> 16, w1 & 0xFFFFu, w1 >> 16};
+  float lo[4], hi[4];
+  bool ok = rscale >= 0x1p-126f && rscale <= 0x1.fffffep127f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t mag = (e[k] & 0x7FFFu) << 16;  // |x| as binary32
+    ok = ok && mag <= 0x7F800000u;                 // not a NaN
+    const uint32_t m = __float_as_uint(__uint_as_float(mag) * rscale);
+    lo[k] = __uint_as_float(min(max(m, 8u) - 8u, kMax));
+    hi[k] = __uint_as_float(min(m + 8u, kMax));
+  }
+  // codes of lo[2h+t], hi[2h+t] in bytes 2t, 2t+1 of d[h]
+  uint32_t d[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int v0 = __builtin_amdgcn_cvt_pk_fp8_f32(lo[2 * h], hi[2 * h], 0, false);
+    d[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(lo[2 * h + 1], hi[2 * h + 1], v0, true);
+    ok = ok && ((d[h] ^ (d[h] >> 8)) & 0x00FF00FFu) == 0;
+  }
+  if (!ok) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) c |= f32_to_fp8_e4m3(bf16_bits_to_f32(e[k]) / scale) << (8 * k);
+    return c;
+  }
+  const uint32_t code = (d[0] & 0xFFu) | ((d[0] >> 8) & 0xFF00u) | ((d[1] & 0xFFu) << 16) | ((d[1] << 8) & 0xFF000000u);
+  const uint32_t sign = ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) | (w1 & 0x80000000u);
+  return code | sign;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }

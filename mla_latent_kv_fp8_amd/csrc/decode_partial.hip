@@ -88,6 +88,63 @@ struct PartialArgs {
   int32_t ws_o_off;     // byte offset of the partial rows [slot][RB][512] bf16 in ws
 };
 
+// The cache write fused into the call (the WRITE variant; empty otherwise,
+// so the plain kernel's arguments do not change).  The batch * k new
+// tokens are the last k of each request: token r * k + j is request r's
+// token L_r - k + j, with bf16 rows c [.][512] and pe [.][64] (16-byte
+// aligned, row strides in elements) and cache slot slot[.] (skipped
+// outside [0, num_slots)).
+template <bool WRITE>
+struct NewArgs {};
+template <>
+struct NewArgs<true> {
+  const uint16_t* c;
+  const uint16_t* pe;
+  int64_t c_r, pe_r;
+  const int64_t* slot;
+  uint8_t* cache;  // the cache, written
+  int32_t k;
+};
+
+// new tokens per request the fused cache write stages in LDS
+constexpr int NEW_MAX = 8;
+
+// The fused cache write for new tokens j0..j1-1 of request r that no piece
+// attends (positions before the request's first token): read, encoded and
+// stored straight from global memory by the first row block's workgroup.
+__device__ __forceinline__ void write_new_direct(const PartialArgs& p, const NewArgs<true>& nw, int r, int j0,
+                                                 int j1, int tid) {
+  for (int i = tid; i < (j1 - j0) * 72; i += 256) {
+    const int64_t t = (int64_t)r * nw.k + j0 + i / 72;
+    const int c8 = i % 72;  // columns 8*c8 .. 8*c8+7
+    const int64_t slot = nw.slot[t];
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const uint16_t* src = c8 < 64 ? nw.c + t * nw.c_r + 8 * c8 : nw.pe + t * nw.pe_r + 8 * (c8 - 64);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+    const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
+    *reinterpret_cast<u32x2*>(nw.cache + slot * MLA_D_QK + 8 * c8) = encode_fp8x8(w, p.kv_scale);
+  }
+}
+
+// The fused cache write of a piece's cnt new tokens, staged in LDS as bf16
+// (latent rows of 1 KB from nraw, then a block of 128-byte rope rows) with
+// their slots (two dwords each) in nslot: encoded and stored, 8 columns per
+// thread and step.
+__device__ __forceinline__ void store_new_rows(const PartialArgs& p, const NewArgs<true>& nw,
+                                               const MLA_LDS uint8_t* nraw, const MLA_LDS int32_t* nslot, int cnt,
+                                               int tid) {
+  const float rscale = 1.0f / p.kv_scale;
+  for (int i = tid; i < cnt * 72; i += 256) {
+    const int jj = i / 72, c8 = i - 72 * jj;  // columns 8*c8 .. 8*c8+7 of staged token jj
+    const int64_t slot = (int64_t)(uint32_t)nslot[2 * jj] | ((int64_t)nslot[2 * jj + 1] << 32);
+    if (slot < 0 || slot >= p.num_slots) continue;
+    const MLA_LDS uint8_t* src = c8 < 64 ? nraw + 1024 * jj + 16 * c8 : nraw + 1024 * NEW_MAX + 128 * jj + 16 * (c8 - 64);
+    const u32x4 raw = *(const MLA_LDS u32x4*)src;
+    *reinterpret_cast<u32x2*>(nw.cache + slot * MLA_D_QK + 8 * c8) =
+        u32x2{encode_fp8x4_fast(raw[0], raw[1], p.kv_scale, rscale), encode_fp8x4_fast(raw[2], raw[3], p.kv_scale, rscale)};
+  }
+}
+
 // The split partition computed on the host (the one the kernel derives from
 // kv_indptr, unit by unit), passed in the kernel arguments: a workgroup then
 // starts its first piece without first reading the request offsets and
@@ -557,8 +614,8 @@ __device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const flo
   }
 }
 
-template <int NRG, bool QF8, bool PLAN, bool FUSE>
-__global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl) {
+template <int NRG, bool QF8, bool PLAN, bool FUSE, bool WRITE>
+__global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl, NewArgs<WRITE> nw) {
   static_assert(!FUSE || PLAN, "the fused call takes the host-built partition");
   constexpr int RB = 16 * NRG;
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_[NBUF * TILE_BYTES];
@@ -573,6 +630,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   __shared__ int64_t rowoff[RB];  // output offset of block row i within its request, -1 past M
   __shared__ int64_t latoff[FUSE ? RB : 1];  // the same in the merged latent
   __shared__ int32_t last_[1];               // fused call: the counter value this block saw
+  // the fused cache write: a piece's new tokens as bf16 (latent rows, then
+  // a block of rope rows) and their slots (two dwords each)
+  __shared__ __attribute__((aligned(16))) uint8_t nraw_[WRITE ? NEW_MAX * 1024 + 1024 : 16];
+  __shared__ __attribute__((aligned(16))) int32_t nslot_[WRITE ? 64 : 1];
   // the normalised O rows are staged as bf16 [RB][O_PITCH] in the tile buffers
   constexpr int O_PITCH = MLA_D_LATENT + 16;  // +32 B: rows start 8 banks apart
   static_assert(RB * O_PITCH * 2 <= NBUF * TILE_BYTES, "O staging fits the tile buffers");
@@ -582,6 +643,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   MLA_LDS uint8_t* kbuf = (MLA_LDS uint8_t*)kbuf_;
   MLA_LDS int32_t* idxl = (MLA_LDS int32_t*)idx;
   MLA_LDS uint8_t* qarea = (MLA_LDS uint8_t*)qarea_;
+  MLA_LDS uint8_t* nraw = (MLA_LDS uint8_t*)nraw_;
+  MLA_LDS int32_t* nslot = (MLA_LDS int32_t*)nslot_;
   const VOffsets vo = v_offsets(wave, lane);
 
   // ---- block -> (worker, row block), from the grid alone, so that no
@@ -737,6 +800,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     const int64_t vq = div_pos(V, chunk);  // the unit that holds it
     if (L == 0) {
       const int64_t owner = vq < nunits - 1 ? vq : nunits - 1;
+      if constexpr (WRITE)
+        if (owner == u && rb == 0) write_new_direct(p, nw, r, 0, nw.k, tid);
       if (owner == u) {
         if constexpr (FUSE) {
           // an empty request's merged rows: latent 0, LSE -inf
@@ -776,6 +841,10 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       continue;
     }
     if (!FUSE && k == 0 && nsplit < p.num_splits) fill_neginf(r, nsplit);
+    // the fused cache write: new tokens before the request's first token
+    // (a request shorter than nw_k) are written by its first piece's owner
+    if constexpr (WRITE)
+      if (a == 0 && rb == 0 && L < nw.k) write_new_direct(p, nw, r, 0, nw.k - L, tid);
 
     // ---------------------------------------------------------- one piece
     const int32_t* rows_r = p.indices + (PLAN ? base + (int)P : p.indptr[r]);
@@ -796,6 +865,33 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // tile 2 is issued only after every wave has read it).  Only the indices
     // are waited for here: tiles 0 and 1 are issued while the query is still
     // in flight.
+    // ---- the fused cache write: this piece's new tokens (the cnt from
+    // nw_j0 on) as bf16 rows, and their slots, to LDS by direct loads
+    // issued ahead of the indices, so the wait for the indices covers them
+    int nw_cnt = 0;
+    bool nw_late = false;  // stored after tiles 0 and 1 are issued (see below)
+    if constexpr (WRITE) {
+      const int pos0 = L - nw.k;  // position of the request's new token 0
+      const int j0 = max(0, a - pos0), j1 = min(nw.k, b - pos0);
+      if (j1 > j0) {
+        nw_cnt = j1 - j0;
+        nw_late = max(pos0, a) - a >= 3 * NT;
+        const int64_t tn = (int64_t)r * nw.k + j0;  // the first of them
+        for (int jj = wave; jj < nw_cnt; jj += 4)
+          lds_dma16(reinterpret_cast<const uint8_t*>(nw.c + (tn + jj) * nw.c_r) + 16 * lane,
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(nraw + 1024 * jj)));
+        if (wave == 0) {
+          // lane l: rope chunk l%8 of token l/8 (lanes past the last token
+          // load its last chunk again); dword l of the slots likewise
+          const int jr = min(lane >> 3, nw_cnt - 1);
+          lds_dma16(reinterpret_cast<const uint8_t*>(nw.pe + (tn + jr) * nw.pe_r) + 16 * (lane & 7),
+                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(nraw + 1024 * NEW_MAX)));
+          lds_dma4(reinterpret_cast<const int32_t*>(nw.slot + tn) + min(lane, 2 * nw_cnt - 1),
+                   __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)nslot));
+        }
+      }
+    }
+
     int64_t rowq[NRG];
 #pragma unroll
     for (int g = 0; g < NRG; ++g) rowq[g] = ((int64_t)r * p.qlen + rj[g]) * p.q_sr + (int64_t)rh[g] * p.q_sh;
@@ -804,6 +900,23 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
     rp_ready = true;  // the planned offsets were loaded before this staging
+    if constexpr (WRITE) {
+      // The new tokens go into their cache slots before any tile that holds
+      // them is loaded, from every row block's workgroup (the same bytes):
+      // the tiles' loads then read them, as this CU's own stores keep its
+      // L1 current and reach the XCD's L2 first.  When tiles 0-2 hold one,
+      // they are stored here and waited for (stores and loads share one
+      // counter, so this also waits for the query); otherwise after tiles 0
+      // and 1 are issued and before tile 2 is: global loads and stores
+      // report completion to a wave in issue order, so the wait for tile 1
+      // (after tile 2 is issued) covers them too, and the barrier after it
+      // comes before tile 3 is issued.
+      if (nw_cnt > 0 && !nw_late) {
+        store_new_rows(p, nw, nraw, nslot, nw_cnt, tid);
+        wait_vm_all();
+        __syncthreads();
+      }
+    }
     {
       const int slen = min(IDX_CAP, b - a);
       const int safe_row = first_valid_row(idx, slen, p.num_slots);
@@ -815,6 +928,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         const bool bad = idx_share_bad(idxl, slen, (uint32_t)p.num_slots, wave, lane);
         if (lane == 0) segbad_[wave] = bad;  // read after the barrier below
       }
+      // the late new rows, encoded while the tiles load (with their stores
+      // the youngest, no more than 9 outstanding still means tile 0 has
+      // landed)
+      if constexpr (WRITE)
+        if (nw_late) store_new_rows(p, nw, nraw, nslot, nw_cnt, tid);
       // the query (issued before the tiles) and tile 0 have landed; tile 1's
       // 9 loads may still fly
       if (slen > NT)
@@ -1128,8 +1246,9 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
 static std::mutex g_time_mu;
 static hipEvent_t g_time_ev[2] = {nullptr, nullptr};
 
-template <int NRG, bool QF8, bool PLAN, bool FUSE = false>
-static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, hipStream_t s) {
+template <int NRG, bool QF8, bool PLAN, bool FUSE = false, bool WRITE = false>
+static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, hipStream_t s,
+                  const NewArgs<WRITE>& nw = NewArgs<WRITE>{}) {
   static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
   const unsigned g = a.num_workers % 8 == 0 ? 8 : 1;
   const dim3 grid(g, (unsigned)a.n_rb, (unsigned)a.num_workers / g);
@@ -1141,9 +1260,9 @@ static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, hipStream_t s)
     g_time_ev[0] = g_time_ev[1] = nullptr;
   }
   if (ev[0] || ev[1])
-    hipExtLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), grid, dim3(256), 0, s, ev[0], ev[1], 0, a, pl);
+    hipExtLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE, WRITE>), grid, dim3(256), 0, s, ev[0], ev[1], 0, a, pl, nw);
   else
-    hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE>), grid, dim3(256), 0, s, a, pl);
+    hipLaunchKernelGGL((partial_kernel<NRG, QF8, PLAN, FUSE, WRITE>), grid, dim3(256), 0, s, a, pl, nw);
   return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -1260,6 +1379,18 @@ static int common_args(PartialArgs& a, int& nrg, const void* q, bool q_fp8, int6
   return MLA_OK;
 }
 
+// the new tokens of the fused cache write (per_request of them for each
+// request, the request's last ones)
+struct NewRows {
+  const uint16_t* kv_c;
+  int64_t kv_c_stride;
+  const uint16_t* k_pe;
+  int64_t k_pe_stride;
+  const int64_t* slots;
+  int32_t per_request;
+  uint8_t* cache;
+};
+
 static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, int64_t q_stride_head,
                                float q_scale, int32_t batch, int32_t qlen, int32_t heads,
                                const uint8_t* kv_cache, int64_t num_slots, const int32_t* kv_indptr,
@@ -1267,9 +1398,18 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
                                int32_t num_splits, int32_t num_workers, int32_t split_min_tokens,
                                uint16_t* o_part, int64_t os_split, int64_t os_row, int64_t os_head,
                                float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
-                               void* stream, const int32_t* indptr_host = nullptr) {
+                               void* stream, const int32_t* indptr_host = nullptr,
+                               const NewRows* nw = nullptr) {
   if (batch < 0 || qlen < 1 || heads < 1 || num_splits < 1 || num_splits > 1024 || num_workers < 1)
     return MLA_ERR_INVALID;
+  if (nw) {
+    if (!nw->kv_c || !nw->k_pe || !nw->slots || nw->kv_c_stride < MLA_D_LATENT || nw->k_pe_stride < MLA_D_ROPE)
+      return MLA_ERR_INVALID;
+    if (nw->per_request < 1 || nw->per_request > NEW_MAX) return MLA_ERR_INVALID;
+    // 16-byte row loads
+    if (((uintptr_t)nw->kv_c | (uintptr_t)nw->k_pe) % 16 != 0 || (nw->kv_c_stride | nw->k_pe_stride) % 8 != 0)
+      return MLA_ERR_UNSUPPORTED;
+  }
   if (batch == 0) return MLA_OK;
   if (!o_part || !lse_part) return MLA_ERR_INVALID;
   PartialArgs a;
@@ -1290,32 +1430,36 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
            ? make_plan(indptr_host, batch, num_splits, num_workers, split_min_tokens, pl)
            : MLA_ERR_UNSUPPORTED;
   if (st == MLA_ERR_INVALID) return st;
+  const bool wr = nw != nullptr;
+  NewArgs<true> nwa{};
+  if (nw) nwa = NewArgs<true>{nw->kv_c, nw->k_pe, nw->kv_c_stride, nw->k_pe_stride, nw->slots, nw->cache,
+                              nw->per_request};
   if (st == MLA_OK) {
     if (q_fp8) {
       switch (nrg) {
-        case 1: return launch<1, true, true>(a, pl, s);
-        case 2: return launch<2, true, true>(a, pl, s);
-        default: return launch<3, true, true>(a, pl, s);
+        case 1: return wr ? launch<1, true, true, false, true>(a, pl, s, nwa) : launch<1, true, true>(a, pl, s);
+        case 2: return wr ? launch<2, true, true, false, true>(a, pl, s, nwa) : launch<2, true, true>(a, pl, s);
+        default: return wr ? launch<3, true, true, false, true>(a, pl, s, nwa) : launch<3, true, true>(a, pl, s);
       }
     }
     switch (nrg) {
-      case 1: return launch<1, false, true>(a, pl, s);
-      case 2: return launch<2, false, true>(a, pl, s);
-      default: return launch<3, false, true>(a, pl, s);
+      case 1: return wr ? launch<1, false, true, false, true>(a, pl, s, nwa) : launch<1, false, true>(a, pl, s);
+      case 2: return wr ? launch<2, false, true, false, true>(a, pl, s, nwa) : launch<2, false, true>(a, pl, s);
+      default: return wr ? launch<3, false, true, false, true>(a, pl, s, nwa) : launch<3, false, true>(a, pl, s);
     }
   }
   const UnitPlan<false> none;
   if (q_fp8) {
     switch (nrg) {
-      case 1: return launch<1, true, false>(a, none, s);
-      case 2: return launch<2, true, false>(a, none, s);
-      default: return launch<3, true, false>(a, none, s);
+      case 1: return wr ? launch<1, true, false, false, true>(a, none, s, nwa) : launch<1, true, false>(a, none, s);
+      case 2: return wr ? launch<2, true, false, false, true>(a, none, s, nwa) : launch<2, true, false>(a, none, s);
+      default: return wr ? launch<3, true, false, false, true>(a, none, s, nwa) : launch<3, true, false>(a, none, s);
     }
   }
   switch (nrg) {
-    case 1: return launch<1, false, false>(a, none, s);
-    case 2: return launch<2, false, false>(a, none, s);
-    default: return launch<3, false, false>(a, none, s);
+    case 1: return wr ? launch<1, false, false, false, true>(a, none, s, nwa) : launch<1, false, false>(a, none, s);
+    case 2: return wr ? launch<2, false, false, false, true>(a, none, s, nwa) : launch<2, false, false>(a, none, s);
+    default: return wr ? launch<3, false, false, false, true>(a, none, s, nwa) : launch<3, false, false>(a, none, s);
   }
 }
 
@@ -1462,6 +1606,38 @@ extern "C" int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_str
                                   kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
                                   ls_split, ls_row, ls_head, stream, kv_indptr_host);
+}
+
+extern "C" int mla_kv_write_decode_partial_hostplan(
+    const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe, int64_t k_pe_stride,
+    const int64_t* slot_mapping, int32_t new_per_request, const uint16_t* q, int64_t q_stride_row,
+    int64_t q_stride_head, int32_t batch, int32_t qlen, int32_t heads, uint8_t* kv_cache, int64_t num_slots,
+    const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float kv_scale, int32_t num_splits,
+    int32_t num_workers, int32_t split_min_tokens, uint16_t* o_part, int64_t os_split, int64_t os_row,
+    int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+    const int32_t* kv_indptr_host, void* stream) {
+  if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
+  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request, kv_cache};
+  return mla::decode_partial_impl(q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
+                                  num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream, kv_indptr_host, &nw);
+}
+
+extern "C" int mla_kv_write_decode_partial_fp8q_hostplan(
+    const uint16_t* kv_c, int64_t kv_c_stride, const uint16_t* k_pe, int64_t k_pe_stride,
+    const int64_t* slot_mapping, int32_t new_per_request, const uint8_t* q8, int64_t q_stride_row,
+    int64_t q_stride_head, float q_scale, int32_t batch, int32_t qlen, int32_t heads, uint8_t* kv_cache,
+    int64_t num_slots, const int32_t* kv_indptr, const int32_t* kv_indices, float sm_scale, float kv_scale,
+    int32_t num_splits, int32_t num_workers, int32_t split_min_tokens, uint16_t* o_part, int64_t os_split,
+    int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
+    const int32_t* kv_indptr_host, void* stream) {
+  if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
+  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request, kv_cache};
+  return mla::decode_partial_impl(q8, true, q_stride_row, q_stride_head, q_scale, batch, qlen, heads,
+                                  kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
+                                  num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
+                                  ls_split, ls_row, ls_head, stream, kv_indptr_host, &nw);
 }
 
 extern "C" int64_t mla_decode_attend_workspace_bytes(int32_t batch, int32_t qlen, int32_t heads, int32_t num_workers) {

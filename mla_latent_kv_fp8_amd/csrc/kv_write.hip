@@ -35,17 +35,7 @@ __global__ void __launch_bounds__(256) kv_write_kernel(const uint16_t* __restric
   }
   const int64_t slot = slots[i];
   if (slot < 0 || slot >= num_slots) return;
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float x = bf16_bits_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    uint32_t b = f32_to_fp8_e4m3(x / kv_scale);  // correctly rounded binary32 division
-    if (e < 4)
-      lo |= b << (8 * e);
-    else
-      hi |= b << (8 * (e - 4));
-  }
-  *reinterpret_cast<u32x2*>(cache + slot * MLA_D_QK + c0) = u32x2{lo, hi};
+  *reinterpret_cast<u32x2*>(cache + slot * MLA_D_QK + c0) = encode_fp8x8(w, kv_scale);
 }
 
 // One thread per 8 consecutive columns of one (row, head) query vector:

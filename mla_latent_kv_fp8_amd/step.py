@@ -7,7 +7,9 @@ query with concat_quant_fp8 each step and attends on the fp8 codes
 place of merge_lse + value_gate (the value heads must be the attention
 heads); `fused_attend = True` runs decode_attend (the partials and their
 merge in one launch, into self.latent) in place of decode_partial +
-merge_lse.  The partials come from the *_hostplan entry points (the split
+merge_lse; `fused_write = True` runs kv_write_decode_partial_hostplan (the
+cache write of the new tokens inside the partials' launch) in place of
+kv_write + decode_partial.  The partials come from the *_hostplan entry points (the split
 partition built on the host from the request offsets) unless `host_plan` is
 set to False, which calls mla_decode_partial(_fp8q); the two give the same
 bits.
@@ -22,7 +24,7 @@ import numpy as np
 import torch
 
 from . import (D_LATENT, D_QK, D_V, concat_quant_fp8, decode_attend, decode_attend_workspace_bytes, decode_partial,
-               kv_write, merge_lse, merge_value_gate, value_gate)
+               kv_write, kv_write_decode_partial_hostplan, merge_lse, merge_value_gate, value_gate)
 from .synth import FP8_NAN, Workload
 
 
@@ -47,6 +49,8 @@ class DeviceStep:
         self.fused_post = False
         # run() attends and merges in one launch (decode_attend, bf16 query)
         self.fused_attend = False
+        # run() writes the new tokens inside the partials' launch
+        self.fused_write = False
         self.workspace = None  # decode_attend's workspace, allocated (zeroed) on first use
         self.kv_cache = torch.full((w.num_slots, D_QK), FP8_NAN, dtype=torch.uint8, device=dev)
         self.indptr = torch.from_numpy(w.indptr).to(dev)
@@ -93,13 +97,30 @@ class DeviceStep:
         nr = self.new_rows
         kv_write(nr[:, :D_LATENT], nr[:, D_LATENT:], self.slot_mapping, self.kv_cache, self.w.kv_scale)
 
-    def attend(self):
+    def attend(self, write_new: bool = False):
+        """The split-KV partials; write_new: with the new tokens' cache write
+        in the same launch (host plan only)."""
         w = self.w
+        if write_new:
+            if not self.host_plan:
+                raise ValueError("the fused cache write takes the host-built partition")
+            nr = self.new_rows
+            kv_write_decode_partial_hostplan(
+                nr[:, :D_LATENT], nr[:, D_LATENT:], self.slot_mapping, self.q, self.kv_cache, self.indptr,
+                self.indices, self.o_part, self.lse_part, self.indptr_host, qlen=w.qlen, heads=w.heads,
+                sm_scale=w.sm_scale, kv_scale=w.kv_scale, num_workers=self.num_workers,
+                split_min_tokens=self.split_min, q_scale=self.q_scale)
+            return
         plan = self.indptr_host if self.host_plan else None
         decode_partial(self.q, self.kv_cache, self.indptr, self.indices, self.o_part, self.lse_part,
                        qlen=w.qlen, heads=w.heads, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
                        num_workers=self.num_workers, split_min_tokens=self.split_min, q_scale=self.q_scale,
                        kv_indptr_host=plan)
+
+    def partials(self):
+        """The step's partial launch: with the new tokens' cache write in it
+        when fused_write is set (run() then writes no rows before it)."""
+        self.attend(write_new=self.fused_write and not self.fused_attend)
 
     def attend_merged(self):
         """The partials and their LSE merge in one launch: self.latent (the
@@ -132,7 +153,8 @@ class DeviceStep:
                          w_fp4=self.w_fp4, w_scale=self.w_scale, lse=self.lse)
 
     def run(self, write_new: bool = True):
-        if write_new:
+        fused_write = write_new and self.fused_write and not self.fused_attend
+        if write_new and not fused_write:
             self.write_new_tokens()
         if self.q_bf16 is not None:
             self.quantize_query()
@@ -142,7 +164,7 @@ class DeviceStep:
             self.attend_merged()
             self.value()
             return
-        self.attend()
+        self.partials()
         if self.fused_post:
             self.merge_value()
         else:

@@ -243,6 +243,44 @@ def test_hostplan_partition_runs_on_the_host(mlib):
                                              null) == 1
 
 
+def test_fused_write_argument_errors(mlib):
+    # the cache write fused into the partials' launch: its own arguments are
+    # checked before anything is enqueued, also for batch = 0
+    import torch
+
+    L = mlib.lib()
+    null = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced by the rejected cases
+    ih = np.array([0, 40, 90], dtype=np.int32)
+
+    def call(kv_c=fake, kv_c_stride=512, k_pe=fake, k_pe_stride=64, slots=fake, k=1, batch=2, fp8=False,
+             host=ih.ctypes.data_as(ctypes.c_void_p)):
+        new = (kv_c, kv_c_stride, k_pe, k_pe_stride, slots, k)
+        if fp8:
+            return L.mla_kv_write_decode_partial_fp8q_hostplan(*new, fake, 576, 576, 0.5, batch, 1, 16, fake, 10,
+                                                               fake, fake, 0.1, 1.0, 2, 8, 1, fake, 0, 0, 0, fake,
+                                                               0, 0, 0, host, null)
+        return L.mla_kv_write_decode_partial_hostplan(*new, fake, 576, 576, batch, 1, 16, fake, 10, fake, fake, 0.1,
+                                                      1.0, 2, 8, 1, fake, 0, 0, 0, fake, 0, 0, 0, host, null)
+
+    for fp8 in (False, True):
+        assert call(k=0, fp8=fp8) == 1
+        assert call(k=9, fp8=fp8) == 1
+        assert call(k=0, batch=0, fp8=fp8) == 1
+        assert call(kv_c=null, fp8=fp8) == 1
+        assert call(k_pe=null, fp8=fp8) == 1
+        assert call(slots=null, fp8=fp8) == 1
+        assert call(kv_c_stride=511, fp8=fp8) == 1
+        assert call(k_pe_stride=63, fp8=fp8) == 1
+        assert call(host=null, fp8=fp8) == 1
+        assert call(kv_c=ctypes.c_void_p((1 << 20) + 8), fp8=fp8) == 2  # not 16-byte aligned
+        assert call(k_pe_stride=68, fp8=fp8) == 2                        # rows 8 bytes apart
+        assert call(batch=0, k=8, fp8=fp8) == 0                          # no requests: a no-op
+        if torch.cuda.device_count() == 0:
+            # valid arguments reach the launch, which fails without a device
+            assert call(k=8, fp8=fp8) == 3
+
+
 def test_absorb_query_argument_errors(mlib):
     L = mlib.lib()
     null = ctypes.c_void_p(0)
