@@ -3,9 +3,10 @@
 A step is the whole hot path over one batch of synthetic input already
 resident in HBM: kv_write (the step's new tokens) -> decode_partial ->
 merge_lse -> value_gate, where the cache write runs inside the partials'
-launch (mla_kv_write_decode_partial_hostplan) when each request has one new
-token (--write auto; measured faster there, and slower with 4 or 8 new
-tokens per request, whose encodes every row block's workgroup repeats).
+launch (mla_kv_write_decode_partial_hostplan) when each request has at most 4 new
+tokens (--write auto: every workload but spec_q8).  Measured, the fused
+steps are 2-8 us faster; with spec_q8's 8 new tokens per request, whose
+encodes every row block's workgroup repeats, it comes out even.
 Default workload: the batch-decode configuration
 (64 requests, qlen 1, 96 heads in a 128-head query buffer, fp8 KV with
 kv_scale 0.05, context lengths uniform in [1024, 8192], 4 empty requests,
@@ -81,7 +82,7 @@ def parse():
     ap.add_argument("--write", choices=("auto", "fused", "separate"), default="auto",
                     help="the new tokens' cache write inside the partials' launch "
                          "(mla_kv_write_decode_partial_hostplan) or as mla_kv_write before it; auto: fused "
-                         "for one new token per request (measured faster there), separate for more")
+                         "for up to 4 new tokens per request (measured faster there), separate for more")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-config-rooflines", action="store_true",
                     help="skip the partial kernel's rooflines on the other configurations")
@@ -377,7 +378,8 @@ def main():
         # 1/16 for the N(0,1) synthetic query), then attends on the fp8 codes
         st.use_fp8_query(1.0 / 16.0)
     st.fused_post = fused_post = args.post == "fused" and w.value_heads == w.heads
-    st.fused_write = fused_write = args.write == "fused" or (args.write == "auto" and w.qlen == 1)
+    new_per_request = len(w.slot_mapping) // w.batch
+    st.fused_write = fused_write = args.write == "fused" or (args.write == "auto" and new_per_request <= 4)
     evict = Evict(torch)
     torch.cuda.synchronize()
 
