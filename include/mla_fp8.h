@@ -290,9 +290,9 @@ int mla_decode_partial_fp8q_hostplan(const uint8_t* q8, int64_t q_stride_row, in
  *                normally names slot_mapping[r * k + j]).  A token at a
  *                negative position (L_r < k) is written and not attended.
  *   kv_c, k_pe   16-byte aligned, strides multiples of 8 elements.
- * Each workgroup that attends a new token writes that token's row itself
- * before it loads any cache row of its piece, so the launch needs no
- * ordering between workgroups.  In return, a slot this call writes must be
+ * Each workgroup that attends a new token writes that token's row itself,
+ * and has the store completed before it loads the tile that holds the
+ * token, so the launch needs no ordering between workgroups.  In return, a slot this call writes must be
  * named in kv_indices at no position other than its own token's (as a slot
  * freshly given to a request is); where it is, which row such a read sees
  * is unspecified.  Slots must be distinct, as for mla_kv_write; a slot
