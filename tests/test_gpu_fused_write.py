@@ -67,6 +67,8 @@ CASES = [  # name, batch, lengths, workers, split_min
     ("spec_q8", 3, (30, 900), 8, 16),
     ("rank_share", 6, (50, 1500), 8, 1),
     ("batch", 2, (5000, 6000), 2, 1),  # one piece per request, three index segments
+    ("batch", 12, (60, 3000), 300, 1),  # more workers than the host plan takes: the in-kernel partition
+    ("spec_q4", 5, (40, 900), 300, 1),
 ]
 
 
