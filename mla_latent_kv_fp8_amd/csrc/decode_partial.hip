@@ -358,16 +358,18 @@ __device__ __forceinline__ MLA_LDS uint8_t* q_block(MLA_LDS uint8_t* buf2, MLA_L
 // blocks, all by direct global->LDS loads; returns how many of this wave's
 // loads are the query's (the caller waits for the indices alone first).
 // rowq[g]: offset of this lane's row (g, lr) in the query (elements).
-template <int NRG, bool QF8>
+template <int NRG, bool QF8, class AfterIdx>
 __device__ __forceinline__ int stage_q_and_idx(const PartialArgs& p, const int64_t (&rowq)[NRG],
                                                const int32_t* idx_src, int nidx, MLA_LDS uint8_t* buf2,
                                                MLA_LDS uint8_t* qarea, MLA_LDS int32_t* idx_lds, int wave,
-                                               int lane) {
+                                               int lane, AfterIdx after_idx) {
   constexpr int NT_G = QF8 ? 9 : 18;  // blocks per row group
   const int lg = lane >> 4;
   // the indices go first: the caller waits for them alone and issues the
-  // first tiles while the query is still in flight
+  // first tiles while the query is still in flight; after_idx issues loads
+  // the same wait covers (the returned count is the query's loads only)
   stage_idx(idx_src, nidx, idx_lds, wave, lane);
+  after_idx();
   int n = 0;
 #pragma unroll
   for (int g = 0; g < NRG; ++g) {
@@ -801,7 +803,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     if (L == 0) {
       const int64_t owner = vq < nunits - 1 ? vq : nunits - 1;
       if constexpr (WRITE)
-        if (owner == u && rb == 0) write_new_direct(p, nw, r, 0, nw.k, tid);
+        if (__builtin_expect(owner == u && rb == 0, 0)) write_new_direct(p, nw, r, 0, nw.k, tid);
       if (owner == u) {
         if constexpr (FUSE) {
           // an empty request's merged rows: latent 0, LSE -inf
@@ -844,7 +846,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // the fused cache write: new tokens before the request's first token
     // (a request shorter than nw_k) are written by its first piece's owner
     if constexpr (WRITE)
-      if (a == 0 && rb == 0 && L < nw.k) write_new_direct(p, nw, r, 0, nw.k - L, tid);
+      if (__builtin_expect(a == 0 && rb == 0 && L < nw.k, 0)) write_new_direct(p, nw, r, 0, nw.k - L, tid);
 
     // ---------------------------------------------------------- one piece
     const int32_t* rows_r = p.indices + (PLAN ? base + (int)P : p.indptr[r]);
@@ -865,18 +867,25 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     // tile 2 is issued only after every wave has read it).  Only the indices
     // are waited for here: tiles 0 and 1 are issued while the query is still
     // in flight.
-    // ---- the fused cache write: this piece's new tokens (the cnt from
-    // nw_j0 on) as bf16 rows, and their slots, to LDS by direct loads
-    // issued ahead of the indices, so the wait for the indices covers them
-    int nw_cnt = 0;
+    // ---- the fused cache write: this piece's new tokens (nw_cnt of them,
+    // from request token j0 on) as bf16 rows, and their slots, to LDS by
+    // direct loads issued between the indices and the query, so the wait
+    // for the indices covers them
+    int nw_cnt = 0, nw_j0 = 0;
     bool nw_late = false;  // stored after tiles 0 and 1 are issued (see below)
     if constexpr (WRITE) {
       const int pos0 = L - nw.k;  // position of the request's new token 0
       const int j0 = max(0, a - pos0), j1 = min(nw.k, b - pos0);
       if (j1 > j0) {
         nw_cnt = j1 - j0;
+        nw_j0 = j0;
         nw_late = max(pos0, a) - a >= 3 * NT;
-        const int64_t tn = (int64_t)r * nw.k + j0;  // the first of them
+      }
+    }
+    auto stage_new = [&]() {
+      if constexpr (WRITE) {
+        if (nw_cnt == 0) return;
+        const int64_t tn = (int64_t)r * nw.k + nw_j0;  // the first of them
         for (int jj = wave; jj < nw_cnt; jj += 4)
           lds_dma16(reinterpret_cast<const uint8_t*>(nw.c + (tn + jj) * nw.c_r) + 16 * lane,
                     __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(nraw + 1024 * jj)));
@@ -890,13 +899,13 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
                    __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)nslot));
         }
       }
-    }
+    };
 
     int64_t rowq[NRG];
 #pragma unroll
     for (int g = 0; g < NRG; ++g) rowq[g] = ((int64_t)r * p.qlen + rj[g]) * p.q_sr + (int64_t)rh[g] * p.q_sh;
     const int nq = stage_q_and_idx<NRG, QF8>(p, rowq, rows_r + a, min(IDX_CAP, b - a), kbuf + 2 * TILE_BYTES, qarea,
-                                             idxl, wave, lane);
+                                             idxl, wave, lane, stage_new);
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
     rp_ready = true;  // the planned offsets were loaded before this staging
@@ -911,7 +920,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       // report completion to a wave in issue order, so the wait for tile 1
       // (after tile 2 is issued) covers them too, and the barrier after it
       // comes before tile 3 is issued.
-      if (nw_cnt > 0 && !nw_late) {
+      if (__builtin_expect(nw_cnt > 0 && !nw_late, 0)) {
         store_new_rows(p, nw, nraw, nslot, nw_cnt, tid);
         wait_vm_all();
         __syncthreads();
