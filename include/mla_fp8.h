@@ -195,8 +195,7 @@ int mla_concat_quant_fp8(const uint16_t* ql_nope, int64_t ln_row, int64_t ln_hea
  * positive and finite; MLA_ERR_UNSUPPORTED unless q is 16-byte aligned with strides
  * that are multiples of 8, o_part is 8-byte aligned with strides that are
  * multiples of 4 and kv_cache is 16-byte aligned, or when qlen * heads
- * exceeds 2^20 or num_workers exceeds one launch grid (524280 when it is a
- * multiple of 8, else 65535).
+ * exceeds 2^20 or num_workers exceeds one launch grid (524280).
  */
 int mla_decode_partial(const uint16_t* q, int64_t q_stride_row, int64_t q_stride_head,
                        int32_t batch, int32_t qlen, int32_t heads, const uint8_t* kv_cache,

@@ -649,13 +649,14 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   MLA_LDS int32_t* nslot = (MLA_LDS int32_t*)nslot_;
   const VOffsets vo = v_offsets(wave, lane);
 
-  // ---- block -> (worker, row block), from the grid alone, so that no
-  // argument read waits for another: the grid is (g, row blocks, workers /
-  // g), g = 8 when num_workers is a multiple of 8, else 1.  Workgroups go to
-  // the 8 XCDs round robin in linear order (x first), so with g = 8 the row
+  // ---- block -> (worker, row block), from the block indices alone, so
+  // that no argument read waits for another (the grid's size is an
+  // argument read too): the grid is (8, row blocks, ceil(workers / 8)), and
+  // the workgroups past the last worker find no unit and leave.  Workgroups
+  // go to the 8 XCDs round robin in linear order (x first), so the row
   // blocks of a worker (linear ids 8 apart) share an XCD and its L2, start
   // together, and workers interleave across the XCDs.
-  const int u = blockIdx.x + gridDim.x * blockIdx.z, rb = blockIdx.y;
+  const int u = blockIdx.x + 8 * blockIdx.z, rb = blockIdx.y;
 
   // ---- the split partition: T, L_max -> chunk, and the requests this
   // unit covers
@@ -666,14 +667,23 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   __shared__ __attribute__((aligned(16))) int32_t rPraw[PLAN_RP];
   int base = 0, r = 0, r_end = 0, nreq = 0;
   int64_t Tv = 0, chunk = 1, nunits = 1;
+  int plan_p0 = 0, plan_len0 = 0;  // the first piece's offset and length, from the plan
   if constexpr (PLAN) {
     base = pl.base;
     Tv = pl.Tv;
     chunk = pl.chunk;
     nunits = pl.nunits;
+    // this unit's plan entries, read with the other arguments (u < 8 *
+    // ceil(workers / 8) <= PLAN_UNITS), and all used here, so that none of
+    // the reads is left for later: the first piece's cache indices wait on
+    // plan_p0 and plan_len0
+    const int plan_r = pl.r[u], plan_n = pl.nreq[u];
+    plan_p0 = pl.p0[u];
+    plan_len0 = pl.len0[u];
+    asm volatile("" ::"s"(plan_r), "s"(plan_n), "s"(plan_p0), "s"(plan_len0));
     if (u < nunits) {
-      r = pl.r[u];
-      r_end = r + pl.nreq[u];
+      r = plan_r;
+      r_end = r + plan_n;
       // kv_indptr[r + i] (i < PLAN_RP, clamped to the last entry) to LDS by
       // direct loads; the first piece takes its offsets from the plan, and
       // these loads, issued before its staging, have landed by its first wait
@@ -775,8 +785,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     int L;
     if constexpr (PLAN) {
       if (ri == 0) {
-        P = pl.p0[u];
-        L = pl.len0[u];
+        P = plan_p0;
+        L = plan_len0;
       } else {
         if (!rp_ready) {  // the first piece was empty: wait for the offsets here
           wait_vm_all();
@@ -1259,8 +1269,7 @@ template <int NRG, bool QF8, bool PLAN, bool FUSE = false, bool WRITE = false>
 static int launch(const PartialArgs& a, const UnitPlan<PLAN>& pl, hipStream_t s,
                   const NewArgs<WRITE>& nw = NewArgs<WRITE>{}) {
   static_assert(sizeof(PartialArgs) + sizeof(UnitPlan<PLAN>) <= 4096, "kernel arguments over 4 KB");
-  const unsigned g = a.num_workers % 8 == 0 ? 8 : 1;
-  const dim3 grid(g, (unsigned)a.n_rb, (unsigned)a.num_workers / g);
+  const dim3 grid(8, (unsigned)a.n_rb, ((unsigned)a.num_workers + 7) / 8);
   hipEvent_t ev[2];
   {
     std::lock_guard<std::mutex> lock(g_time_mu);
@@ -1374,8 +1383,8 @@ static int common_args(PartialArgs& a, int& nrg, const void* q, bool q_fp8, int6
   // rows per block: 16, 32 or 48 (larger requests take several blocks)
   nrg = M <= 16 ? 1 : (M <= 32 ? 2 : 3);
   const int n_rb = (int)((M + 16 * nrg - 1) / (16 * nrg));
-  // the grid is (g, n_rb, num_workers / g), g = 8 or 1 (n_rb <= 21846 here)
-  if (num_workers / (num_workers % 8 == 0 ? 8 : 1) > 65535) return MLA_ERR_UNSUPPORTED;
+  // the grid is (8, n_rb, ceil(num_workers / 8)) (n_rb <= 21846 here)
+  if (((int64_t)num_workers + 7) / 8 > 65535) return MLA_ERR_UNSUPPORTED;
   a = PartialArgs{};
   a.q = q_fp8 ? nullptr : (const uint16_t*)q;
   a.q8 = q_fp8 ? (const uint8_t*)q : nullptr;

@@ -102,8 +102,8 @@ def test_argument_errors_before_device_work(mlib):
         assert L.mla_decode_partial(*sc(sm, kv)) == 1                 # scales must be positive and finite
     gw = lambda nw: (fake, 576, 576, 2, 1, 16, fake, 10, fake, fake, 0.1, 1.0, 2, nw, 1, fake, 0, 0, 0, fake, 0,
                      0, 0, null)
-    assert L.mla_decode_partial(*gw(524288)) == 2   # workers / 8 = 65536: past one launch grid
-    assert L.mla_decode_partial(*gw(65537)) == 2    # not a multiple of 8, so one worker per z: past 65535
+    assert L.mla_decode_partial(*gw(524288)) == 2   # ceil(workers / 8) = 65536: past one launch grid
+    assert L.mla_decode_partial(*gw(524281)) == 2   # also 65536 (the last z holds one worker)
     cq = lambda qs, lr, rows: (fake, lr, 512, fake, 192 * 4, 192, qs, rows, 4, fake, 2304, 576, null)
     assert L.mla_concat_quant_fp8(*cq(0.5, 2048, 0)) == 0            # rows = 0: no-op
     assert L.mla_concat_quant_fp8(null, 2048, 512, null, 768, 192, 0.5, 2, 4, null, 2304, 576, null) == 1
