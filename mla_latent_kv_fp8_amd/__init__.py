@@ -82,6 +82,15 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
+def use_library(path: str) -> None:
+    """Load another build of the same library on the first call into it (a
+    measurement build such as libmla_fp8_timeline.so); call before that."""
+    global LIB_PATH
+    if _lib is not None:
+        raise MlaError("the library is already loaded from %s" % LIB_PATH)
+    LIB_PATH = path
+
+
 def _check(status: int, what: str) -> None:
     if status != 0:
         raise MlaError("%s: %s" % (what, lib().mla_status_string(status).decode()))

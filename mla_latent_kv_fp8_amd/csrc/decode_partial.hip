@@ -616,6 +616,32 @@ __device__ __forceinline__ void p_tile(const f32x4 (&S)[NRG], float c, const flo
   }
 }
 
+// Per-workgroup wall-clock marks of the partial kernel, in the measurement
+// build libmla_fp8_timeline.so only (compiled with MLA_WG_TIMELINE; the
+// marks compile to nothing otherwise): s_memrealtime, a 100 MHz counter
+// common to every CU, at
+//   0 the workgroup's start, 1 its end, 2 (a count) its pieces,
+//   3 / 7 the start of its first / second piece, 4 / 8 their first ready
+//   tile (staged and waited for), 5 / 9 the end of their tile loop (the
+//   last pass's, after a restart), 6 / 10 (a count) their tiles,
+//   11, 12, 13 in its last piece's epilogue: row sums and maxima exchanged,
+//   rows normalised into LDS, partial rows stored,
+//   14 the late new rows of the fused cache write encoded and stored (first
+//   piece), 15 the first piece's cache indices landed.
+// Workgroup record i is linear block id i; mla_wg_timeline reads them.
+#ifdef MLA_WG_TIMELINE
+constexpr bool kTimeline = true;
+constexpr int TL_MAX = 4096;  // workgroups with a record
+__device__ uint64_t g_timeline[TL_MAX][16];
+#else
+constexpr bool kTimeline = false;
+#endif
+__device__ __forceinline__ uint64_t tl_now() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t));
+  return t;
+}
+
 template <int NRG, bool QF8, bool PLAN, bool FUSE, bool WRITE>
 __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan<PLAN> pl, NewArgs<WRITE> nw) {
   static_assert(!FUSE || PLAN, "the fused call takes the host-built partition");
@@ -648,6 +674,19 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
   MLA_LDS uint8_t* nraw = (MLA_LDS uint8_t*)nraw_;
   MLA_LDS int32_t* nslot = (MLA_LDS int32_t*)nslot_;
   const VOffsets vo = v_offsets(wave, lane);
+  uint64_t tl[kTimeline ? 16 : 1] = {};  // the timeline marks (measurement build)
+  int tl_piece = 0;
+  // mark i of the first piece, or i + 4 of the second (constant indices:
+  // the marks stay in registers)
+  auto tl_piece_mark = [&](int i, uint64_t v, bool add) {
+    if constexpr (kTimeline) {
+      if (tl_piece == 0)
+        tl[i] = add ? tl[i] + v : v;
+      else if (tl_piece == 1)
+        tl[i + 4] = add ? tl[i + 4] + v : v;
+    }
+  };
+  if constexpr (kTimeline) tl[0] = tl_now();
 
   // ---- block -> (worker, row block), from the block indices alone, so
   // that no argument read waits for another (the grid's size is an
@@ -859,6 +898,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       if (__builtin_expect(a == 0 && rb == 0 && L < nw.k, 0)) write_new_direct(p, nw, r, 0, nw.k - L, tid);
 
     // ---------------------------------------------------------- one piece
+    if constexpr (kTimeline) tl_piece_mark(3, tl_now(), false);
+    bool tl_ready = false;
     const int32_t* rows_r = p.indices + (PLAN ? base + (int)P : p.indptr[r]);
     int lim[NRG];  // visible tokens of row (g, lr), as an end in request tokens
     int lim_min = b;
@@ -919,6 +960,8 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     wait_vm_upto(__builtin_amdgcn_readfirstlane(nq));
     __syncthreads();
     rp_ready = true;  // the planned offsets were loaded before this staging
+    if constexpr (kTimeline)
+      if (tl_piece == 0) tl[15] = tl_now();
     if constexpr (WRITE) {
       // The new tokens go into their cache slots before any tile that holds
       // them is loaded, from every row block's workgroup (the same bytes):
@@ -951,7 +994,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       // the youngest, no more than 9 outstanding still means tile 0 has
       // landed)
       if constexpr (WRITE)
-        if (nw_late) store_new_rows(p, nw, nraw, nslot, nw_cnt, tid);
+        if (nw_late) {
+          store_new_rows(p, nw, nraw, nslot, nw_cnt, tid);
+          if constexpr (kTimeline)
+            if (tl_piece == 0) tl[14] = tl_now();
+        }
       // the query (issued before the tiles) and tile 0 have landed; tile 1's
       // 9 loads may still fly
       if (slen > NT)
@@ -1034,6 +1081,11 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       // the masking path (which then finds it); written before the barrier
       // that follows tile 0's wait
       const bool seg_bad = (segbad_[0] | segbad_[1] | segbad_[2] | segbad_[3]) != 0;
+      if constexpr (kTimeline) {
+        if (!tl_ready) tl_piece_mark(4, tl_now(), false);
+        tl_ready = true;
+        tl_piece_mark(6, (uint64_t)ntiles, true);
+      }
       // P^T is double buffered by tile parity.
       for (int it = 0; it < ntiles; ++it) {
         const int t0 = s0 + NT * it;
@@ -1098,6 +1150,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
         pv_tile<NRG>(kt, ptb, O, v0, vo, lane);
       }
     }
+    if constexpr (kTimeline) tl_piece_mark(5, tl_now(), false);
     // ---- end of the piece: the row sums and maxima of the four quarters;
     // rows whose maximum lies more than 64 log2 units from their reference
     // take it as the new reference and the piece runs again (a block-uniform
@@ -1112,6 +1165,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       }
     }
     __syncthreads();
+    if constexpr (kTimeline) tl[11] = tl_now();
     bool moved = false;
 #pragma unroll
     for (int g = 0; g < NRG; ++g) {
@@ -1128,6 +1182,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
       restaged = true;
     }
     }  // while (again)
+    if constexpr (kTimeline) ++tl_piece;
 
     // ---------------------------------------------------- piece epilogue
     // The row sums; O normalised to bf16 into LDS (every wave is past its
@@ -1176,6 +1231,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     }
     __syncthreads();
     {
+      if constexpr (kTimeline) tl[12] = tl_now();
       // this wave's rows wave, wave+4, ...: all LDS reads first, then the stores
       uint16_t* obase = FUSE ? p.lat + (int64_t)r * p.qlen * p.lat_r + 8 * lane
                              : p.o + k * p.os_s + (int64_t)r * p.qlen * p.os_r + 8 * lane;
@@ -1202,6 +1258,7 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
                                                    0, 17);
       }
     }
+    if constexpr (kTimeline) tl[13] = tl_now();
     if constexpr (FUSE) {
       if (!direct) {
         // Count this piece in once its rows are complete in memory (every
@@ -1258,6 +1315,13 @@ __global__ void __launch_bounds__(256, 1) partial_kernel(PartialArgs p, UnitPlan
     }
     __syncthreads();
   }
+#ifdef MLA_WG_TIMELINE
+  tl[1] = tl_now();
+  tl[2] = (uint64_t)tl_piece;
+  const unsigned lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  if (tid == 0 && lin < TL_MAX)
+    for (int i = 0; i < 16; ++i) g_timeline[lin][i] = tl[i];
+#endif
 }
 
 // The events that the next launch of the partial kernel records at its own
@@ -1700,3 +1764,21 @@ extern "C" int mla_time_next_partial(void* start_event, void* stop_event) {
   mla::g_time_ev[1] = (hipEvent_t)stop_event;
   return MLA_OK;
 }
+
+#ifdef MLA_WG_TIMELINE
+// The measurement build's timeline (the marks described at g_timeline):
+// records 0 .. n-1 (n <= 4096) to host memory, 16 uint64 each; and a clear
+// of every record (a workgroup that finds no unit writes none).  Both wait
+// for the device.
+extern "C" int mla_wg_timeline(uint64_t* host, int32_t n) {
+  if (!host || n < 0 || n > mla::TL_MAX) return MLA_ERR_INVALID;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(mla::g_timeline), sizeof(uint64_t) * 16 * (size_t)n) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+extern "C" int mla_wg_timeline_clear() {
+  static uint64_t zero[mla::TL_MAX][16];
+  return hipMemcpyToSymbol(HIP_SYMBOL(mla::g_timeline), zero, sizeof(zero)) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+#endif

@@ -301,3 +301,15 @@ def test_absorb_query_argument_errors(mlib):
     assert call(qn_row=260) == 2               # bf16 rows in 16-byte chunks
     assert call(wk_n=66) == 2                  # W_K code words are 4-byte aligned
     assert call(fp8=1, out_row=1160) == 2      # fp8 output rows in 16-byte chunks
+
+
+def test_timeline_build_exports_its_reader(mlib):
+    # the measurement build carries the partial kernel's per-workgroup marks
+    # and their reader; the product library has neither
+    from mla_latent_kv_fp8_amd import build
+
+    if not os.path.exists(build.TIMELINE_LIB):
+        pytest.skip("the timeline build is not built (python -m mla_latent_kv_fp8_amd.build --timeline)")
+    T = ctypes.CDLL(build.TIMELINE_LIB)
+    assert hasattr(T, "mla_wg_timeline") and hasattr(T, "mla_wg_timeline_clear")
+    assert not hasattr(mlib.lib(), "mla_wg_timeline")
