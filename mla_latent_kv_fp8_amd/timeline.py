@@ -5,11 +5,12 @@ workgroup's start and end, at the phases of its first two pieces and of its
 last epilogue (csrc/decode_partial.hip lists them at g_timeline).
 
     python -m mla_latent_kv_fp8_amd.build --timeline
-    python -m mla_latent_kv_fp8_amd.timeline [--config batch] [--write separate|fused] [--launches 3]
+    python -m mla_latent_kv_fp8_amd.timeline [--config batch] [--write separate|fused] [--launches 3] [--warm]
 
 Each timed launch follows 0.1 s of back-to-back launches (the clocks up)
 and a read of a separate 512 MiB buffer (L2 and the Infinity Cache then
-hold nothing of the launch).  One JSON line per launch: times in us from
+hold nothing of the launch); --warm leaves that read out, so the launch
+finds in the caches what the one before it left.  One JSON line per launch: times in us from
 the first workgroup's start, means over the workgroups unless named
 otherwise.  The marks cost a few instructions each, so the launch runs a
 little slower than the plain build's.
@@ -80,6 +81,7 @@ def main() -> None:
     ap.add_argument("--write", choices=("separate", "fused"), default="separate",
                     help="the plain partial launch, or the one with the new tokens' cache write in it")
     ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--warm", action="store_true", help="no eviction read before the timed launch")
     args = ap.parse_args()
     use_library(_build.TIMELINE_LIB)
     L = lib()
@@ -100,8 +102,8 @@ def main() -> None:
     n = 8 * ((st.num_workers + 7) // 8) * n_rb  # every workgroup of the launch grid
     if n > 4096:
         raise SystemExit("the launch has %d workgroups; the timeline holds 4096" % n)
-    print(json.dumps({"config": args.config, "write": args.write, "workers": st.num_workers, "row_blocks": n_rb}),
-          flush=True)
+    print(json.dumps({"config": args.config, "write": args.write, "warm": args.warm, "workers": st.num_workers,
+                      "row_blocks": n_rb}), flush=True)
     for _ in range(args.launches):
         t_end = time.perf_counter() + 0.1
         while time.perf_counter() < t_end:
@@ -110,7 +112,11 @@ def main() -> None:
                 st.partials()
             torch.cuda.synchronize()
         assert L.mla_wg_timeline_clear() == 0
-        evict.sum()
+        if not args.warm:
+            evict.sum()
+        else:
+            st.partials()  # the launch before the timed one, with nothing between them
+            torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         st.partials()
