@@ -93,7 +93,9 @@ struct PartialArgs {
 // tokens are the last k of each request: token r * k + j is request r's
 // token L_r - k + j, with bf16 rows c [.][512] and pe [.][64] (16-byte
 // aligned, row strides in elements) and cache slot slot[.] (skipped
-// outside [0, num_slots)).
+// outside [0, num_slots)).  The rows go to the cache the call reads
+// (PartialArgs::kv, written through cache_w): no pointer of their own, one
+// scalar pair fewer for the argument reads to compete for.
 template <bool WRITE>
 struct NewArgs {};
 template <>
@@ -102,9 +104,11 @@ struct NewArgs<true> {
   const uint16_t* pe;
   int64_t c_r, pe_r;
   const int64_t* slot;
-  uint8_t* cache;  // the cache, written
   int32_t k;
 };
+
+// the cache the fused write stores to: the one the call reads
+__device__ __forceinline__ uint8_t* cache_w(const PartialArgs& p) { return const_cast<uint8_t*>(p.kv); }
 
 // new tokens per request the fused cache write stages in LDS
 constexpr int NEW_MAX = 8;
@@ -122,7 +126,7 @@ __device__ __forceinline__ void write_new_direct(const PartialArgs& p, const New
     const uint16_t* src = c8 < 64 ? nw.c + t * nw.c_r + 8 * c8 : nw.pe + t * nw.pe_r + 8 * (c8 - 64);
     const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
     const uint32_t w[4] = {raw[0], raw[1], raw[2], raw[3]};
-    *reinterpret_cast<u32x2*>(nw.cache + slot * MLA_D_QK + 8 * c8) = encode_fp8x8(w, p.kv_scale);
+    *reinterpret_cast<u32x2*>(cache_w(p) + slot * MLA_D_QK + 8 * c8) = encode_fp8x8(w, p.kv_scale);
   }
 }
 
@@ -140,7 +144,7 @@ __device__ __forceinline__ void store_new_rows(const PartialArgs& p, const NewAr
     if (slot < 0 || slot >= p.num_slots) continue;
     const MLA_LDS uint8_t* src = c8 < 64 ? nraw + 1024 * jj + 16 * c8 : nraw + 1024 * NEW_MAX + 128 * jj + 16 * (c8 - 64);
     const u32x4 raw = *(const MLA_LDS u32x4*)src;
-    *reinterpret_cast<u32x2*>(nw.cache + slot * MLA_D_QK + 8 * c8) =
+    *reinterpret_cast<u32x2*>(cache_w(p) + slot * MLA_D_QK + 8 * c8) =
         u32x2{encode_fp8x4_fast(raw[0], raw[1], p.kv_scale, rscale), encode_fp8x4_fast(raw[2], raw[3], p.kv_scale, rscale)};
   }
 }
@@ -1462,7 +1466,7 @@ static int common_args(PartialArgs& a, int& nrg, const void* q, bool q_fp8, int6
 }
 
 // the new tokens of the fused cache write (per_request of them for each
-// request, the request's last ones)
+// request, the request's last ones), written to the call's kv_cache
 struct NewRows {
   const uint16_t* kv_c;
   int64_t kv_c_stride;
@@ -1470,7 +1474,6 @@ struct NewRows {
   int64_t k_pe_stride;
   const int64_t* slots;
   int32_t per_request;
-  uint8_t* cache;
 };
 
 static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, int64_t q_stride_head,
@@ -1514,8 +1517,7 @@ static int decode_partial_impl(const void* q, bool q_fp8, int64_t q_stride_row, 
   if (st == MLA_ERR_INVALID) return st;
   const bool wr = nw != nullptr;
   NewArgs<true> nwa{};
-  if (nw) nwa = NewArgs<true>{nw->kv_c, nw->k_pe, nw->kv_c_stride, nw->k_pe_stride, nw->slots, nw->cache,
-                              nw->per_request};
+  if (nw) nwa = NewArgs<true>{nw->kv_c, nw->k_pe, nw->kv_c_stride, nw->k_pe_stride, nw->slots, nw->per_request};
   if (st == MLA_OK) {
     if (q_fp8) {
       switch (nrg) {
@@ -1699,7 +1701,7 @@ extern "C" int mla_kv_write_decode_partial_hostplan(
     int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
     const int32_t* kv_indptr_host, void* stream) {
   if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
-  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request, kv_cache};
+  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request};
   return mla::decode_partial_impl(q, false, q_stride_row, q_stride_head, 1.0f, batch, qlen, heads, kv_cache,
                                   num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
@@ -1715,7 +1717,7 @@ extern "C" int mla_kv_write_decode_partial_fp8q_hostplan(
     int64_t os_row, int64_t os_head, float* lse_part, int64_t ls_split, int64_t ls_row, int64_t ls_head,
     const int32_t* kv_indptr_host, void* stream) {
   if (!kv_indptr_host && batch > 0) return MLA_ERR_INVALID;
-  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request, kv_cache};
+  const mla::NewRows nw{kv_c, kv_c_stride, k_pe, k_pe_stride, slot_mapping, new_per_request};
   return mla::decode_partial_impl(q8, true, q_stride_row, q_stride_head, q_scale, batch, qlen, heads,
                                   kv_cache, num_slots, kv_indptr, kv_indices, sm_scale, kv_scale, num_splits,
                                   num_workers, split_min_tokens, o_part, os_split, os_row, os_head, lse_part,
